@@ -1,0 +1,36 @@
+"""CPU oracle for the GEMM hot path. TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The GPU library never calls it and shares no code with
+it: the two meet only in the seeded inputs (package `synth`) they both read.
+
+What it computes (in float64, the plain definition written out):
+
+    acc[m, n] = sum_k a(m, k) * b(k, n)                 (float64)
+    dq        = scale_a[m] * scale_b[n] * acc           (FP8 variant only)
+    z         = alpha * dq + beta * C_in[m, n] + bias[n]
+    y         = act(z)
+    out       = round_to_nearest_even(y) in FP32 or BF16 (single rounding)
+
+Sources: the GEMM definition C = alpha*A*B + beta*C with A MxK, B KxN (first
+DeepGEMM page, sec. 1.1); FP32-or-better accumulation of 16-bit inputs (same
+page, sec. 3.1); bias, then activation, then the output write, fused into the
+epilogue (same page, sec. 6.1); per-token (row of A) and per-channel (column
+of B) scales applied after accumulation and before the store (DeepGEMM: FP8
+precision Tensor Core GEMM optimisation, sec. 1.2 and 3.2); the E4M3 format
+(same page, sec. 1.2); element-by-element CPU comparison (the CUDA-tile GEMM
+tutorial page, sec. 6).
+
+Parity status: every function here is pinned by the `-m "not gpu"` tests in
+tests/test_oracle.py (codec tables, rounding ties, integer-valued exact
+products, identity and permutation matrices, closed forms, linearity, GELU
+against tabulated normal-CDF values). No function is "parity unpinned".
+"""
+from .codecs import (decode_bf16, decode_e4m3, round_to_bf16, round_to_bf16_bits,
+                     round_to_f32)
+from .gemm import activation, gemm_bf16, gemm_fp8_scaled, logical_a, logical_b
+
+__all__ = [
+    "decode_bf16", "decode_e4m3", "round_to_bf16", "round_to_bf16_bits", "round_to_f32",
+    "activation", "gemm_bf16", "gemm_fp8_scaled", "logical_a", "logical_b",
+]

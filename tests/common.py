@@ -1,0 +1,43 @@
+"""Test helpers: run the oracle on a synth.Problem and compare results with it."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from tests import tolerance
+
+
+def reference(p, rows=None, cols=None):
+    """(y, out) from the oracle for problem p, optionally on a row/column sample."""
+    if p.kind == "bf16":
+        return oracle.gemm_bf16(p.M, p.N, p.K, p.alpha, p.A, p.layout_a, p.B, p.layout_b,
+                                p.beta, p.C, p.c_dtype, p.bias, p.act, rows=rows, cols=cols)
+    return oracle.gemm_fp8_scaled(p.M, p.N, p.K, p.alpha, p.A, p.layout_a, p.B, p.layout_b,
+                                  p.scale_a, p.scale_b, p.beta, p.C, p.c_dtype, p.bias, p.act,
+                                  rows=rows, cols=cols)
+
+
+def operand_norms(p, rows=None, cols=None):
+    """||a_m||_2 per selected row and ||b_n||_2 per selected column (dequantised)."""
+    dec = oracle.decode_bf16 if p.kind == "bf16" else oracle.decode_e4m3
+    r = np.arange(p.M) if rows is None else np.asarray(rows)
+    c = np.arange(p.N) if cols is None else np.asarray(cols)
+    a = dec(oracle.logical_a(p.A, p.layout_a, p.M, p.K)[r, :])
+    b = dec(oracle.logical_b(p.B, p.layout_b, p.K, p.N)[:, c])
+    rn = np.sqrt((a * a).sum(axis=1))
+    cn = np.sqrt((b * b).sum(axis=0))
+    if p.kind == "fp8":
+        rn = rn * np.asarray(p.scale_a, dtype=np.float64)[r]
+        cn = cn * np.asarray(p.scale_b, dtype=np.float64)[c]
+    return rn, cn
+
+
+def compare(p, out, rows=None, cols=None, what=""):
+    """Check a result (M'xN' array: float32, or uint16 BF16 codes) against the oracle."""
+    y, ref = reference(p, rows, cols)
+    rn, cn = operand_norms(p, rows, cols)
+    what = what or p.name
+    if p.c_dtype == 0:
+        return tolerance.check_f32(out, y, rn, cn, p.alpha, what)
+    return tolerance.check_bf16(oracle.decode_bf16(out), y, oracle.decode_bf16(ref), rn, cn,
+                                p.alpha, p.act, what)
