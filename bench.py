@@ -1,0 +1,283 @@
+"""Benchmark of the GEMM hot path on one MI355X.
+
+One step = one BF16 GEMM at M=N=K=4096 (A row-major, B column-major, beta 0.5
+on an FP32 C, as in the square 4096^3 workload) followed by one FP8-E4M3
+per-token/per-channel scaled GEMM at M=N=K=4096 (bias, GELU, BF16 output).
+`value` is the step's throughput: 2MNK flops of both GEMMs over the time of
+both, in TFLOP/s, inputs resident in HBM. Buffer sets rotate so that every
+call reads operands that are not in the 256 MB MALL.
+
+Also reported (not in `value`): each GEMM's TFLOP/s and fraction of the
+dense MFMA peak, the FP8 4096x7168x2048 projection, decode-shaped skinny GEMMs
+in achieved HBM GB/s, FFN projection shapes, and the ragged 4093^3 shapes.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2516.6, "fp8": 5033.2}  # TFLOP/s, MI355X dense
+HBM_GBPS = 8000.0
+ROTATE_BYTES = 600 << 20  # > 2 x (256 MB MALL + 32 MB L2)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-rotate", action="store_true", help="reuse one buffer set (MALL-hot)")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="short run for rocprofv3 --pmc: a 256 MiB device copy (counter "
+                         "calibration) then 3 launches of each headline GEMM")
+    ap.add_argument("--only", default="", help="comma list of extra groups: decode,ffn,ragged,proj")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Workload:
+    """A problem resident on the GPU in `copies` rotating buffer sets."""
+
+    def __init__(self, p, copies):
+        import torch
+        from tests.gpu_util import to_device
+        self.p = p
+        base = to_device(p)
+        self.sets = [base]
+        for _ in range(copies - 1):
+            self.sets.append({k: (v.clone() if v is not None else None) for k, v in base.items()})
+        import dense_gemm_09_amd as g
+        need = g.workspace_size(p.M, p.N, p.K, p.kind == "fp8")
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
+        self.i = 0
+
+    def nbytes_per_set(self):
+        return sum(v.numel() * v.element_size() for v in self.sets[0].values() if v is not None)
+
+    def __call__(self):
+        from tests.gpu_util import call
+        d = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        call(self.p, d, workspace=self.ws)
+
+
+NO_ROTATE = False
+
+
+def copies_for(p):
+    import numpy as np
+    if NO_ROTATE:
+        return 1
+    per = sum(a.nbytes for a in (p.A, p.B, p.C) if a is not None)
+    return int(max(1, min(24, np.ceil(ROTATE_BYTES / max(per, 1)))))
+
+
+def time_calls(fns, steps, warmup):
+    """Run the callables in order per step; per-callable mean ms from HIP events."""
+    import torch
+    s = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        ev[k][0].record(s)
+        for j, f in enumerate(fns):
+            f()
+            ev[k][j + 1].record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [sum(ev[k][j].elapsed_time(ev[k][j + 1]) for k in range(steps)) / steps
+           for j in range(len(fns))]
+    total = sum(ev[k][0].elapsed_time(ev[k][-1]) for k in range(steps))
+    return per, total, wall
+
+
+def cpu_baseline(bf16_p, fp8_p):
+    """The oracle as it stands on the host: one BF16 and one FP8 4096^3 GEMM on a row sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import oracle  # noqa: F401  (the CPU-baseline leg is the one bench path allowed to use it)
+    from tests.common import reference
+    rows = np.arange(1024)
+    flops = 0
+    t0 = time.perf_counter()
+    for p in (bf16_p, fp8_p):
+        reference(p, rows=rows)
+        flops += 2 * len(rows) * p.N * p.K
+    dt = time.perf_counter() - t0
+    threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"), default=1)
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": "rows 0..1023 of the BF16 and of the FP8 4096^3 GEMM (1/4 of one step), "
+                      f"float64 oracle incl. decode and epilogue, {dt:.1f} s"}
+
+
+def kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm_tile.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "dense_gemm_09_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the BF16 4096^3 kernel from the committed counter
+    summary, or None when the kernel source changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "gemm_tile_bf16_4096_traffic.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    rec = dict(line.split(": ", 1) for line in text.splitlines()
+               if line.startswith(("kernel_source_sha256: ", "traffic_bytes_per_launch: ")))
+    if rec.get("kernel_source_sha256", "").strip() != kernel_source_sha():
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+def pmc_run(p_bf16, p_fp8):
+    """Known-size copy (calibrates FETCH_SIZE / WRITE_SIZE), then the GEMMs."""
+    import torch
+    src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    w_bf16, w_fp8 = Workload(p_bf16, 1), Workload(p_fp8, 1)
+    for _ in range(3):
+        w_bf16()
+        w_fp8()
+    torch.cuda.synchronize()
+    log("[bench] pmc run done: copy 268435456 bytes, 3 x bf16 4096^3, 3 x fp8 4096^3")
+
+
+def main():
+    args = parse()
+    global NO_ROTATE
+    NO_ROTATE = args.no_rotate
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this path has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dense_gemm_09_amd as g
+    from synth import workloads
+    g.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.init()
+
+    log("[bench] generating inputs")
+    p_bf16 = workloads.square_bf16(4096)
+    p_fp8 = workloads.fp8_projection(4096, 4096, 4096, sub=1)
+    if args.pmc_run:
+        pmc_run(p_bf16, p_fp8)
+        return
+    w_bf16 = Workload(p_bf16, copies_for(p_bf16))
+    w_fp8 = Workload(p_fp8, copies_for(p_fp8))
+    log(f"[bench] rotation: bf16 {len(w_bf16.sets)} sets x {w_bf16.nbytes_per_set() / 1e6:.0f} MB, "
+        f"fp8 {len(w_fp8.sets)} x {w_fp8.nbytes_per_set() / 1e6:.0f} MB")
+
+    log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
+    torch.cuda.synchronize()
+    per, total_ms, wall = time_calls([w_bf16, w_fp8], args.steps, args.warmup)
+    torch.cuda.synchronize()
+    ms_step = total_ms / args.steps
+    fl_bf16, fl_fp8 = p_bf16.flops, p_fp8.flops
+    tf_bf16 = fl_bf16 / (per[0] * 1e-3) / 1e12
+    tf_fp8 = fl_fp8 / (per[1] * 1e-3) / 1e12
+    value = (fl_bf16 + fl_fp8) / (ms_step * 1e-3) / 1e12
+    log(f"[bench] bf16 {per[0] * 1e3:.1f} us {tf_bf16:.0f} TF ({tf_bf16 / PEAK['bf16']:.1%}) | "
+        f"fp8 {per[1] * 1e3:.1f} us {tf_fp8:.0f} TF ({tf_fp8 / PEAK['fp8']:.1%})")
+
+    pl_bf16 = g.plan(4096, 4096, 4096, False)
+    roof = {"bound": "mfma", "achieved": round(tf_bf16, 1), "peak": PEAK["bf16"],
+            "unit": "TFLOP/s", "frac": round(tf_bf16 / PEAK["bf16"], 4),
+            "traffic": measured_traffic(),
+            "kernel": f"gemm_tile_kernel<{pl_bf16.tile_m},{pl_bf16.tile_n}> bf16 4096^3",
+            "algorithmic_flops_per_launch": fl_bf16, "avg_launch_us": round(per[0] * 1e3, 2)}
+
+    extra = {"bf16_4096": {"us": round(per[0] * 1e3, 2), "tflops": round(tf_bf16, 1),
+                           "frac_peak": round(tf_bf16 / PEAK["bf16"], 4)},
+             "fp8_4096": {"us": round(per[1] * 1e3, 2), "tflops": round(tf_fp8, 1),
+                          "frac_peak": round(tf_fp8 / PEAK["fp8"], 4)}}
+    del w_bf16, w_fp8
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        only = set(args.only.split(",")) if args.only else {"decode", "ffn", "ragged", "proj"}
+        extra.update(run_extras(only))
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline(p_bf16, p_fp8)
+
+    out = {"metric": "GEMM TFLOPS (2MNK/s) bf16 & fp8 at 4096^3; % of MI355X MFMA peak",
+           "value": round(value, 1), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16+fp8", "data": "synthetic",
+           "config": {"workload": "bf16 GEMM 4096^3 (A row-major, B col-major, beta 0.5, fp32 C) "
+                                  "+ fp8-e4m3 GEMM 4096^3 (per-token/per-channel fp32 scales, "
+                                  "bf16 bias, GELU, bf16 out)",
+                      "M": 4096, "N": 4096, "K": 4096, "parallelism": "single GPU",
+                      "rotating_buffer_sets": True},
+           "roofline": roof, "cpu_baseline": cpu, "extra": extra}
+    print(json.dumps(out), flush=True)
+
+
+def run_extras(only):
+    import torch
+    from synth import workloads
+    res = {}
+
+    def measure(name, p, steps=30, warmup=5, hbm_bytes=None):
+        w = Workload(p, copies_for(p))
+        per, _, _ = time_calls([w], steps, warmup)
+        us = per[0] * 1e3
+        r = {"us": round(us, 2), "tflops": round(p.flops / (us * 1e-6) / 1e12, 1)}
+        if hbm_bytes is not None:
+            r["gbps"] = round(hbm_bytes / (us * 1e-6) / 1e9, 0)
+            r["frac_hbm"] = round(hbm_bytes / (us * 1e-6) / 1e9 / HBM_GBPS, 4)
+        res[name] = r
+        log(f"[bench] {name}: {r}")
+        del w
+        torch.cuda.empty_cache()
+
+    if "proj" in only:
+        measure("fp8_4096x7168x2048", workloads.fp8_projection())
+    if "decode" in only:
+        for kind, M, N in workloads.all_decode():
+            p = workloads.decode(kind, M, N)
+            es = 2 if kind == "bf16" else 1
+            by = N * p.K * es + M * p.K * es + M * N * 2 + (8 * (M + N) if kind == "fp8" else 0)
+            measure(f"decode_{kind}_{M}x{N}x4096", p, hbm_bytes=by)
+    if "ffn" in only:
+        for M in workloads.FFN_M:
+            for N, K in workloads.FFN_SHAPES:
+                measure(f"ffn_bf16_{M}x{N}x{K}", workloads.ffn(M, N, K), steps=10, warmup=3)
+    if "ragged" in only:
+        for kind in ("bf16", "fp8"):
+            for padded in (False, True):
+                p = workloads.ragged(kind, 4093, padded)
+                measure(p.name, p, steps=5, warmup=2)
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+// C ABI: argument validation, launch planning and dispatch.
+//
+// The interface follows the FP8 DeepGEMM page's (sec. 5.1): device pointers,
+// sizes, scale vectors, an optional workspace with a separate size query, a
+// stream, and a status code; all checks run before anything is enqueued. The
+// runtime choice of tile and split from the shape is that page's sec. 5.3
+// advice (tile and pipeline depth picked per shape) made concrete for
+// 256 CUs.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "gemm355.h"
+#include "internal.hpp"
+
+namespace g355 {
+namespace {
+
+constexpr int kCUs = 256;
+constexpr int64_t kMaxDim = int64_t{1} << 30;
+
+struct Candidate {
+  int bm, bn, waves, occupancy;  // occupancy: workgroups per CU (LDS-limited)
+  double efficiency;             // fraction of the CU's MFMA rate a full tile sustains
+};
+
+// 256x256: 128 KB LDS, one workgroup per CU. 256x128: 96 KB, one per CU.
+// 128x128: 64 KB, two per CU.
+constexpr Candidate kCandidates[] = {
+    {256, 256, 8, 1, 0.85},
+    {256, 128, 8, 1, 0.75},
+    {128, 128, 4, 2, 0.70},
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+Plan make_plan(int64_t M, int64_t N, int64_t K, bool fp8) {
+  const int bke = fp8 ? 128 : 64;
+  const double flops_per_clk = fp8 ? 8192.0 : 4096.0;  // per CU, dense
+  const double clk = 2.4e9;
+  const double hbm = 5.0e12;        // bytes/s assumed for split-K partial traffic
+  const double reduce_launch = 4e-6;
+  const int64_t kslices = std::max<int64_t>(1, ceil_div(K, bke));
+
+  Plan best{};
+  double best_t = 1e30;
+  for (const Candidate& c : kCandidates) {
+    const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    for (int s = 1; s <= 16; s *= 2) {
+      if (s > 1 && (K == 0 || s > kslices)) break;
+      const int64_t slices_per_split = ceil_div(kslices, s);
+      const int64_t splits = ceil_div(kslices, slices_per_split);  // non-empty partitions
+      if (splits != s) continue;
+      const int64_t wgs = tiles * s;
+      const int64_t slots = int64_t{kCUs} * c.occupancy;
+      const double rounds = static_cast<double>(ceil_div(wgs, slots));
+      const double tile_time = 2.0 * c.bm * c.bn * slices_per_split * bke /
+                               (flops_per_clk * c.efficiency / c.occupancy) / clk;
+      double t = rounds * tile_time;
+      if (s > 1) t += 2.0 * s * static_cast<double>(M) * N * 4 / hbm + reduce_launch;
+      if (t < best_t * 0.98) {
+        best_t = t;
+        best.kernel = KERNEL_TILE;
+        best.bm = c.bm;
+        best.bn = c.bn;
+        best.bk = bke;
+        best.waves = c.waves;
+        best.split = s;
+        best.k_split_len = static_cast<int>(slices_per_split * bke);
+        best.grid = wgs;
+        best.workspace = s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
+      }
+    }
+  }
+  if (K == 0) best.k_split_len = bke;
+  return best;
+}
+
+}  // namespace g355
+
+using namespace g355;
+
+namespace {
+
+bool valid_layout(int l) { return l == GEMM_ROW_MAJOR || l == GEMM_COL_MAJOR; }
+bool valid_out(int d) { return d == GEMM_OUT_F32 || d == GEMM_OUT_BF16; }
+bool valid_act(int a) { return a >= GEMM_ACT_NONE && a <= GEMM_ACT_GELU_TANH; }
+
+gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                int64_t lda, int layout_a, const void* B, int64_t ldb, int layout_b,
+                const float* scale_a, const float* scale_b, float beta, void* C, int64_t ldc,
+                int c_dtype, const void* bias, int act, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  // ---- enums and sizes
+  if (!valid_layout(layout_a) || !valid_layout(layout_b) || !valid_out(c_dtype) ||
+      !valid_act(act))
+    return GEMM_ERR_BAD_ENUM;
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return GEMM_ERR_BAD_DIM;
+  if (fp8 && (layout_a != GEMM_ROW_MAJOR || layout_b != GEMM_COL_MAJOR))
+    return GEMM_ERR_UNSUPPORTED;
+  // ---- leading dimensions
+  const int64_t need_lda = layout_a == GEMM_ROW_MAJOR ? K : M;
+  const int64_t need_ldb = layout_b == GEMM_ROW_MAJOR ? N : K;
+  if (lda < std::max<int64_t>(1, need_lda) || ldb < std::max<int64_t>(1, need_ldb) ||
+      ldc < std::max<int64_t>(1, N))
+    return GEMM_ERR_BAD_LD;
+  if (M == 0 || N == 0) return GEMM_OK;
+  // ---- pointers
+  if (C == nullptr) return GEMM_ERR_NULL_POINTER;
+  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL_POINTER;
+  if (fp8 && (scale_a == nullptr || scale_b == nullptr)) return GEMM_ERR_NULL_POINTER;
+
+  const Plan plan = make_plan(M, N, K, fp8);
+  // Every tile size in use is >= 128, so this bounds the grid of any variant.
+  if (((M + 127) / 128) * ((N + 127) / 128) * plan.split > INT32_MAX) return GEMM_ERR_BAD_DIM;
+  if (plan.workspace > 0) {
+    if (workspace == nullptr) return GEMM_ERR_NULL_POINTER;
+    if (workspace_bytes < plan.workspace) return GEMM_ERR_WORKSPACE_TOO_SMALL;
+  }
+
+  // ---- how each operand reaches LDS
+  const int ce = fp8 ? 16 : 8;  // elements per 16-byte chunk
+  auto aligned16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  LaunchSpec spec{};
+  spec.fp8 = fp8;
+  spec.a_kmajor = layout_a == GEMM_ROW_MAJOR;
+  spec.b_kmajor = layout_b == GEMM_COL_MAJOR;
+  spec.out_bf16 = c_dtype == GEMM_OUT_BF16;
+  const bool k_ok = K % ce == 0;
+  spec.loader_a = (spec.a_kmajor && k_ok && lda % ce == 0 && aligned16(A)) ? LOAD_DIRECT
+                                                                            : LOAD_GENERIC;
+  spec.loader_b = (spec.b_kmajor && k_ok && ldb % ce == 0 && aligned16(B)) ? LOAD_DIRECT
+                                                                            : LOAD_GENERIC;
+  if (K == 0) spec.loader_a = spec.loader_b = LOAD_DIRECT;  // nothing is loaded
+
+  Plan p = plan;
+  if (spec.loader_a != LOAD_DIRECT || spec.loader_b != LOAD_DIRECT) {
+    p.bm = 128;
+    p.bn = 128;
+    p.waves = 4;
+  }
+  GemmArgs a{};
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.scale_a = scale_a;
+  a.scale_b = scale_b;
+  a.workspace = static_cast<float*>(workspace);
+  a.lda = lda;
+  a.ldb = ldb;
+  a.ldc = ldc;
+  a.M = static_cast<int>(M);
+  a.N = static_cast<int>(N);
+  a.K = static_cast<int>(K);
+  a.alpha = alpha;
+  a.beta = beta;
+  a.act = act;
+  {
+    const uintptr_t cbase = reinterpret_cast<uintptr_t>(C);
+    const uintptr_t need = c_dtype == GEMM_OUT_F32 ? 16u : 8u;
+    a.c_vec = (cbase % need == 0 && ldc % 4 == 0) ? 1 : 0;
+  }
+  a.split_k = p.split;
+  a.k_split_len = p.k_split_len;
+  a.tiles_m = static_cast<int>((M + p.bm - 1) / p.bm);
+  a.tiles_n = static_cast<int>((N + p.bn - 1) / p.bn);
+  p.grid = static_cast<int64_t>(a.tiles_m) * a.tiles_n * p.split;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_tile(p, spec, a, s) != hipSuccess) return GEMM_ERR_HIP;
+  if (p.split > 1 && launch_splitk_reduce(p, spec, a, s) != hipSuccess) return GEMM_ERR_HIP;
+  return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                      gemm_layout layout_a, const void* B, int64_t ldb, gemm_layout layout_b,
+                      float beta, void* C, int64_t ldc, gemm_out_dtype c_dtype, const void* bias,
+                      gemm_act act, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(false, M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, nullptr, nullptr, beta,
+             C, ldc, c_dtype, bias, act, workspace, workspace_bytes, stream);
+}
+
+gemm_status gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                            int64_t lda, gemm_layout layout_a, const void* B, int64_t ldb,
+                            gemm_layout layout_b, const float* scale_a, const float* scale_b,
+                            float beta, void* C, int64_t ldc, gemm_out_dtype c_dtype,
+                            const void* bias, gemm_act act, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return run(true, M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, scale_a, scale_b, beta,
+             C, ldc, c_dtype, bias, act, workspace, workspace_bytes, stream);
+}
+
+size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int is_fp8) {
+  if (M <= 0 || N <= 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  return make_plan(M, N, K, is_fp8 != 0).workspace;
+}
+
+gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, int is_fp8, gemm_plan_info* out) {
+  if (out == nullptr) return GEMM_ERR_NULL_POINTER;
+  if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return GEMM_ERR_BAD_DIM;
+  const Plan p = make_plan(std::max<int64_t>(M, 1), std::max<int64_t>(N, 1), K, is_fp8 != 0);
+  out->kernel = p.kernel;
+  out->tile_m = p.bm;
+  out->tile_n = p.bn;
+  out->tile_k = p.bk;
+  out->split_k = p.split;
+  out->waves = p.waves;
+  out->grid = (M == 0 || N == 0) ? 0 : p.grid;
+  out->workspace_bytes = (M == 0 || N == 0) ? 0 : p.workspace;
+  return GEMM_OK;
+}
+
+const char* gemm_status_string(gemm_status s) {
+  switch (s) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_NULL_POINTER: return "GEMM_ERR_NULL_POINTER";
+    case GEMM_ERR_BAD_DIM: return "GEMM_ERR_BAD_DIM";
+    case GEMM_ERR_BAD_LD: return "GEMM_ERR_BAD_LD";
+    case GEMM_ERR_BAD_ENUM: return "GEMM_ERR_BAD_ENUM";
+    case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED";
+    case GEMM_ERR_WORKSPACE_TOO_SMALL: return "GEMM_ERR_WORKSPACE_TOO_SMALL";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
+  }
+  return "GEMM_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Shared device-side definitions for the gfx950 GEMM kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace g355 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+#define G355_LDS __attribute__((address_space(3)))
+#define G355_GLOBAL __attribute__((address_space(1)))
+
+enum Act : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_ERF = 2, ACT_GELU_TANH = 3 };
+
+// Everything a GEMM launch needs; passed by value as the kernel argument.
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;
+  const uint16_t* bias;   // BF16[N] or nullptr
+  const float* scale_a;   // FP32[M] (FP8 only)
+  const float* scale_b;   // FP32[N] (FP8 only)
+  float* workspace;       // split-K partials
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+  float alpha, beta;
+  int act;
+  int a_mn_major;         // 1: A stored column-major (M contiguous), read by the generic loader
+  int b_mn_major;         // 1: B stored row-major (N contiguous), read by the generic loader
+  int c_vec;              // 1: C rows allow 4-element vector access (aligned base, ldc % 4 == 0)
+  int split_k;            // number of K partitions
+  int k_split_len;        // elements of K per partition (multiple of the K tile)
+  int tiles_m, tiles_n;
+};
+
+// ---------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// FP32 -> BF16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ---------------------------------------------------------------- epilogue math
+
+__device__ __forceinline__ float apply_act(float z, int act) {
+  if (act == ACT_RELU) return z > 0.f ? z : 0.f;
+  if (act == ACT_GELU_ERF) return 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
+  if (act == ACT_GELU_TANH) {
+    const float c = 0.79788456080286536f;  // sqrt(2/pi)
+    return 0.5f * z * (1.f + tanhf(c * (z + 0.044715f * z * z * z)));
+  }
+  return z;
+}
+
+// ---------------------------------------------------------------- tile scheduling
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
+// XCD b % 8), and each XCD has its own L2. Renumber so that each XCD receives
+// a contiguous range of logical tile ids; with the grouped order below, the
+// tiles of one XCD then share A row-panels and B column-panels in its L2.
+__device__ __forceinline__ int xcd_remap(int b, int nwg) {
+  constexpr int X = 8;
+  const int per = nwg / X, rem = nwg % X;
+  const int x = b % X, i = b / X;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
+// Logical tile id -> (tile_m, tile_n), grouped GROUP_M tile rows at a time,
+// column-major inside a group.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int group_m,
+                                            int& tm, int& tn) {
+  const int per_group = group_m * tiles_n;
+  const int g = t / per_group;
+  const int first_m = g * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int r = t - g * per_group;
+  tm = first_m + r % gm;
+  tn = r / gm;
+}
+
+}  // namespace g355

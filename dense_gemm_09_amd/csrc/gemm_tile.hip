@@ -1,0 +1,613 @@
+// Tiled MFMA GEMM for gfx950: BF16 x BF16 and FP8-E4M3 x FP8-E4M3, FP32 accumulate.
+//
+// The three-level tiling of the first DeepGEMM page (sec. 2.1: an output tile
+// per workgroup, K slices staged in on-chip memory, a register tile per wave),
+// its software pipeline (sec. 3.3: copies of later slices overlap the
+// matrix-core work on the current one; a barrier separates a buffer's last
+// read from its next overwrite, sec. 4.3), its XOR swizzle of the staged
+// tiles (sec. 3.2) and the zero contribution of out-of-range K (sec. 4.3),
+// laid out for CDNA4:
+//
+// * A K slice is ROWB bytes (64 or 128) of every tile row: 32 or 64 BF16, or
+//   64 or 128 FP8 elements, i.e. CPR = ROWB/16 chunks of 16 bytes. Operand
+//   tiles live in LDS as rows of ROWB bytes with chunk c of row r at physical
+//   chunk c ^ swz(r). The MFMA fragment reads (ds_read_b128; lanes 0..31 on 32
+//   consecutive rows, one chunk each) then hit distinct 16-byte slots within
+//   every 8 and every 16 consecutive lanes, so they are conflict-free whether
+//   the LDS serves 128 or 256 bytes of a 128-bit read per cycle.
+// * STAGES slices are in flight in a ring of LDS buffers. K-major operands
+//   with 16-byte aligned rows are copied global -> LDS by global_load_lds_dwordx4
+//   (64 lanes x 16 B into one contiguous 1 KB segment per instruction). The
+//   lane that lands on physical chunk p of row r fetches logical chunk
+//   p ^ swz(r), so the swizzle costs nothing and no VGPRs hold staged data.
+//   Chunks at or past K read a 16-byte block of zeros; rows past M (or N) read
+//   a clamped valid row whose results are never stored. Every iteration issues
+//   the same number of DMA instructions (slices past the end read zeros), so
+//   waiting for the oldest slice is a fixed vmcnt.
+// * Other operands (B row-major, A column-major, or rows that are not 16-byte
+//   aligned) are loaded element-wise into registers and written to the same
+//   swizzled layout after the slice's MFMAs.
+// * BF16 uses v_mfma_f32_32x32x16_bf16; FP8 uses v_mfma_scale_f32_32x32x64_f8f6f4
+//   with the E4M3 format code and the neutral block scale 2^0 (E8M0 code 127).
+//   The per-token / per-channel scales are FP32 and applied in the epilogue.
+//   A and B fragments put the same K indices in the same register slots, so the
+//   result does not depend on how the hardware orders K inside one MFMA.
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace g355 {
+
+// A 16-byte block of zeros in global memory, read by loads whose chunk lies
+// at or past the end of K.
+__device__ __attribute__((aligned(16))) uint32_t g_zero16[4] = {0u, 0u, 0u, 0u};
+
+// Physical chunk offset of row r for CPR chunks per row (see file comment).
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+template <int BM_, int BN_, int WM_, int WN_, bool FP8_, int ROWB_, int STAGES_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, ROWB = ROWB_, STAGES = STAGES_;
+  static constexpr bool FP8 = FP8_;
+  static constexpr int NWAVES = WM * WN;
+  static constexpr int NT = NWAVES * 64;
+  static constexpr int ES = FP8 ? 1 : 2;      // bytes per element
+  static constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
+  static constexpr int BKE = ROWB / ES;       // K elements per slice
+  static constexpr int CE = 16 / ES;          // K elements per chunk
+  static constexpr int RPS = 1024 / ROWB;     // rows per 1 KB DMA segment
+  static constexpr int A_BYTES = BM * ROWB;
+  static constexpr int B_BYTES = BN * ROWB;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int WTM = BM / WM;         // wave tile
+  static constexpr int WTN = BN / WN;
+  static constexpr int FM = WTM / 32;         // 32x32 MFMA blocks per wave
+  static constexpr int FN = WTN / 32;
+  // MFMA k-steps per slice: BF16 32x32x16 eats 32 B of a row, FP8 32x32x64 64 B.
+  static constexpr int KSTEPS = FP8 ? ROWB / 64 : ROWB / 32;
+  static_assert(ROWB == 64 || ROWB == 128, "row bytes");
+  static_assert(KSTEPS >= 1, "k steps");
+  static_assert((BM / RPS) % NWAVES == 0 && (BN / RPS) % NWAVES == 0, "DMA segments per wave");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
+};
+
+// ------------------------------------------------------------------ DMA loader
+
+template <class C, int ROWS>
+struct DirectLoader {
+  static constexpr int IPW = ROWS / C::RPS / C::NWAVES;  // 1 KB segments per wave per slice
+  const char* src[IPW];                                 // row start + chunk offset (k excluded)
+  int kc[IPW];                                          // first K element of the lane's chunk
+
+  __device__ __forceinline__ void init(const void* base, int64_t ld, int row0, int rows, int wave,
+                                       int lane) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int s = wave * IPW + i;
+      const int r = C::RPS * s + lane / C::CPR;
+      const int c = (lane % C::CPR) ^ swz<C::CPR>(r);
+      int g = row0 + r;
+      g = g < rows ? g : rows - 1;
+      src[i] = static_cast<const char*>(base) + (static_cast<int64_t>(g) * ld) * C::ES + c * 16;
+      kc[i] = c * C::CE;
+    }
+  }
+
+  __device__ __forceinline__ void issue(char* lds_tile, int wave, int k0, int k_end) const {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int s = wave * IPW + i;
+      const char* g = (k0 + kc[i] < k_end) ? src[i] + static_cast<int64_t>(k0) * C::ES
+                                           : reinterpret_cast<const char*>(g_zero16);
+      __builtin_amdgcn_global_load_lds((const G355_GLOBAL void*)(g),
+                                       (G355_LDS void*)(lds_tile + s * 1024), 16, 0, 0);
+    }
+  }
+};
+
+// ------------------------------------------------------------- register loader
+
+template <class C, int ROWS>
+struct GenericLoader {
+  static constexpr int CHUNKS = ROWS * C::CPR;
+  static constexpr int ITEMS = (CHUNKS + C::NT - 1) / C::NT;  // 16-byte chunks per thread
+  uint32_t v[ITEMS][4];
+  const char* base;
+  int64_t ld;
+  int row0, rows;
+  bool kmajor;
+
+  __device__ __forceinline__ bool item(int j, int tid, int& r, int& c) const {
+    const int q = tid + C::NT * j;
+    if (kmajor) { r = q / C::CPR; c = q % C::CPR; }
+    else        { r = q % ROWS; c = q / ROWS; }
+    return q < CHUNKS;
+  }
+
+  __device__ __forceinline__ void load(int tid, int k0, int k_end) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      int r, c;
+      const bool in = item(j, tid, r, c);
+      const int g = row0 + r;
+      const bool row_ok = in && g < rows;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < C::CE; ++e) {
+        const int k = k0 + c * C::CE + e;
+        uint32_t x = 0u;
+        if (row_ok && k < k_end) {
+          const int64_t off = kmajor ? static_cast<int64_t>(g) * ld + k
+                                     : static_cast<int64_t>(k) * ld + g;
+          if constexpr (C::ES == 2) x = reinterpret_cast<const uint16_t*>(base)[off];
+          else x = reinterpret_cast<const uint8_t*>(base)[off];
+        }
+        w[(e * C::ES) >> 2] |= x << (((e * C::ES) & 3) * 8);
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) v[j][d] = w[d];
+    }
+  }
+
+  __device__ __forceinline__ void store(char* lds_tile, int tid) const {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      int r, c;
+      if (!item(j, tid, r, c)) continue;
+      uint4 val = make_uint4(v[j][0], v[j][1], v[j][2], v[j][3]);
+      *reinterpret_cast<uint4*>(lds_tile + r * C::ROWB + ((c ^ swz<C::CPR>(r)) << 4)) = val;
+    }
+  }
+};
+
+// ------------------------------------------------------------ MFMA schedule
+
+// Instruction order for one slice: the first k-step's fragment reads, then
+// each k-step's MFMAs interleaved one-for-one with the next k-step's reads, so
+// the LDS latency of a k-step hides behind the previous k-step's MFMAs.
+// (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read.)
+template <int KSTEPS, int READS, int MFMAS>
+__device__ __forceinline__ void pipeline_hint() {
+  __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+#pragma unroll
+  for (int t = 0; t < KSTEPS; ++t) {
+    if (t + 1 < KSTEPS) {
+#pragma unroll
+      for (int q = 0; q < (READS < MFMAS ? READS : MFMAS); ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if constexpr (READS < MFMAS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
+      else if constexpr (READS > MFMAS) __builtin_amdgcn_sched_group_barrier(0x100, READS - MFMAS, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, 0);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ epilogue
+
+// Output tile epilogue for one wave, staged through LDS so that global C
+// traffic is row-contiguous: the wave writes one 32-row strip of its
+// accumulators (all FN column blocks) into a private LDS area, then reads it
+// back with each lane holding 4 consecutive columns of one row, and applies
+//   v = act(alpha * scale_a[m] * scale_b[n] * acc + beta * C_in[m,n] + bias[n])
+// on float4 / 4-wide BF16 vectors. MFMA 32x32 accumulator layout: element e of
+// lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32 of its 32x32 block.
+// The LDS row stride is WTN+8 floats, which puts the two half-waves of an
+// accumulator write (rows 4 apart) in opposite halves of the 64 banks.
+template <class C>
+struct EpiLayout {
+  static constexpr int STR = C::WTN + 8;            // floats per LDS row
+  static constexpr int WAVE_BYTES = 32 * STR * 4;   // one strip
+  static constexpr int CG = C::WTN / 4;             // lanes per row (4 columns each)
+  static constexpr int RPI = 64 / CG;               // rows per read instruction
+  static constexpr int ITERS = 32 / RPI;
+  static constexpr int TOTAL = C::NWAVES * WAVE_BYTES;
+  static_assert(64 % CG == 0, "lanes per row");
+};
+
+template <class C, bool OUT_BF16, bool SPLIT, int ACT>
+__device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[C::FM][C::FN],
+                                         float* lds, int row0, int col0, int lane, int split) {
+  using E = EpiLayout<C>;
+  const int M = p.M, N = p.N;
+  const int half = lane >> 5;
+  const int cq = lane % E::CG;   // column group of this lane
+  const int rq = lane / E::CG;   // row within a read instruction
+  const int n = col0 + 4 * cq;
+  const bool vec_ok = p.c_vec != 0 && n + 3 < N;
+
+  // Per-column factors, fixed for this lane.
+  float sb[4] = {1.f, 1.f, 1.f, 1.f}, bias_v[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (!SPLIT) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (n + q < N) {
+        if constexpr (C::FP8) sb[q] = p.scale_b[n + q];
+        if (p.bias) bias_v[q] = bf16_bits_to_f32(p.bias[n + q]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
+    // accumulators of rows 32i..32i+31 -> LDS strip
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        lds[(8 * (e >> 2) + 4 * half + (e & 3)) * E::STR + 32 * j + (lane & 31)] = acc[i][j][e];
+
+    float4 cin[E::ITERS];
+    if constexpr (!SPLIT) {
+      if (p.beta != 0.f) {
+#pragma unroll
+        for (int it = 0; it < E::ITERS; ++it) {
+          const int m = row0 + 32 * i + it * E::RPI + rq;
+          cin[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (m >= M) continue;
+          const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
+          if (vec_ok) {
+            if constexpr (OUT_BF16) {
+              const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.C) + off);
+              cin[it] = make_float4(__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xffff0000u),
+                                    __uint_as_float(h.y << 16), __uint_as_float(h.y & 0xffff0000u));
+            } else {
+              cin[it] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.C) + off);
+            }
+          } else {
+            float t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (n + q < N)
+                t[q] = OUT_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.C)[off + q])
+                                : static_cast<const float*>(p.C)[off + q];
+            cin[it] = make_float4(t[0], t[1], t[2], t[3]);
+          }
+        }
+      }
+    }
+
+#pragma unroll
+    for (int it = 0; it < E::ITERS; ++it) {
+      const int r = it * E::RPI + rq;
+      const int m = row0 + 32 * i + r;
+      const float4 a4 = *reinterpret_cast<const float4*>(lds + r * E::STR + 4 * cq);
+      if (m >= M) continue;
+      float v[4] = {a4.x, a4.y, a4.z, a4.w};
+      if constexpr (SPLIT) {
+        float* w = p.workspace + (static_cast<int64_t>(split) * M + m) * N + n;
+        if (vec_ok && (N & 3) == 0) {
+          *reinterpret_cast<float4*>(w) = a4;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) w[q] = v[q];
+        }
+        continue;
+      } else {
+        const float sa = C::FP8 ? p.scale_a[m] : 1.f;
+        const float c4[4] = {cin[it].x, cin[it].y, cin[it].z, cin[it].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float z = v[q];
+          if constexpr (C::FP8) z = z * (sa * sb[q]);
+          z = p.alpha * z;
+          if (p.beta != 0.f) z += p.beta * c4[q];
+          v[q] = apply_act(z + bias_v[q], ACT);
+        }
+        const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
+        if (vec_ok) {
+          if constexpr (OUT_BF16) {
+            uint2 h;
+            h.x = static_cast<uint32_t>(f32_to_bf16_bits(v[0])) |
+                  (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+            h.y = static_cast<uint32_t>(f32_to_bf16_bits(v[2])) |
+                  (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.C) + off) = h;
+          } else {
+            *reinterpret_cast<float4*>(static_cast<float*>(p.C) + off) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (n + q >= N) continue;
+            if constexpr (OUT_BF16) static_cast<uint16_t*>(p.C)[off + q] = f32_to_bf16_bits(v[q]);
+            else static_cast<float*>(p.C)[off + q] = v[q];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------- the kernel
+
+template <class C, int LA, int LB, bool OUT_BF16, bool SPLIT>
+__global__ void __launch_bounds__(C::NT)
+gemm_tile_kernel(GemmArgs p) {
+  // The LDS block holds the ring of K slices, and after the main loop the
+  // epilogue's staging strips.
+  constexpr int LDS_BYTES = C::STAGES * C::STAGE > EpiLayout<C>::TOTAL ? C::STAGES * C::STAGE
+                                                                       : EpiLayout<C>::TOTAL;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // ---- which tile and which K range
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = L / tiles;
+  int tm, tn;
+  tile_coords(L - split * tiles, p.tiles_m, p.tiles_n, 4, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int k_begin = split * p.k_split_len;
+  const int k_end = min(p.K, k_begin + p.k_split_len);
+  const int nk = k_end > k_begin ? (k_end - k_begin + C::BKE - 1) / C::BKE : 0;
+
+  // ---- loaders
+  DirectLoader<C, C::BM> da;
+  DirectLoader<C, C::BN> db;
+  GenericLoader<C, C::BM> ga;
+  GenericLoader<C, C::BN> gb;
+  if constexpr (LA == LOAD_DIRECT) {
+    da.init(p.A, p.lda, m0, p.M, wave, lane);
+  } else {
+    ga.base = static_cast<const char*>(p.A); ga.ld = p.lda; ga.row0 = m0; ga.rows = p.M;
+    ga.kmajor = p.a_mn_major == 0;
+  }
+  if constexpr (LB == LOAD_DIRECT) {
+    db.init(p.B, p.ldb, n0, p.N, wave, lane);
+  } else {
+    gb.base = static_cast<const char*>(p.B); gb.ld = p.ldb; gb.row0 = n0; gb.rows = p.N;
+    gb.kmajor = p.b_mn_major == 0;
+  }
+  constexpr int DMA_PER_SLICE = (LA == LOAD_DIRECT ? DirectLoader<C, C::BM>::IPW : 0) +
+                                (LB == LOAD_DIRECT ? DirectLoader<C, C::BN>::IPW : 0);
+  constexpr int DMA_BEHIND = DMA_PER_SLICE * (C::STAGES - 2);
+
+  auto a_tile = [&](int st) { return smem + st * C::STAGE; };
+  auto b_tile = [&](int st) { return smem + st * C::STAGE + C::A_BYTES; };
+
+  auto fetch = [&](int st, int k0) {
+    if constexpr (LA == LOAD_DIRECT) da.issue(a_tile(st), wave, k0, k_end);
+    else ga.load(tid, k0, k_end);
+    if constexpr (LB == LOAD_DIRECT) db.issue(b_tile(st), wave, k0, k_end);
+    else gb.load(tid, k0, k_end);
+  };
+  auto commit = [&](int st) {
+    if constexpr (LA != LOAD_DIRECT) ga.store(a_tile(st), tid);
+    if constexpr (LB != LOAD_DIRECT) gb.store(b_tile(st), tid);
+  };
+
+  // ---- per-lane fragment addresses (bytes inside a tile)
+  const int wm0 = (wave / C::WN) * C::WTM;
+  const int wn0 = (wave % C::WN) * C::WTN;
+  const int sw = swz<C::CPR>(lane & 31);  // a lane's rows all share their low 5 bits
+  const int half = lane >> 5;
+  const int a_row = (wm0 + (lane & 31)) * C::ROWB;
+  const int b_row = (wn0 + (lane & 31)) * C::ROWB;
+
+  f32x16 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // All fragment reads of a slice are issued first, then its MFMAs: the LDS
+  // latency of later k-steps hides behind the MFMAs of earlier ones.
+  auto compute = [&](int st) {
+    const char* at = a_tile(st);
+    const char* bt = b_tile(st);
+    if constexpr (!C::FP8) {
+      bf16x8 af[C::KSTEPS][C::FM], bfr[C::KSTEPS][C::FN];
+#pragma unroll
+      for (int t = 0; t < C::KSTEPS; ++t) {
+        const int co = ((2 * t + half) ^ sw) << 4;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+          af[t][i] = *reinterpret_cast<const bf16x8*>(at + a_row + i * 32 * C::ROWB + co);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          bfr[t][j] = *reinterpret_cast<const bf16x8*>(bt + b_row + j * 32 * C::ROWB + co);
+      }
+#pragma unroll
+      for (int t = 0; t < C::KSTEPS; ++t)
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t][i], bfr[t][j], acc[i][j],
+                                                                0, 0, 0);
+      pipeline_hint<C::KSTEPS, C::FM + C::FN, C::FM * C::FN>();
+    } else {
+      i32x8 af[C::KSTEPS][C::FM], bfr[C::KSTEPS][C::FN];
+#pragma unroll
+      for (int t = 0; t < C::KSTEPS; ++t) {
+        const int c0 = 4 * t + 2 * half;
+        const int co0 = (c0 ^ sw) << 4;
+        const int co1 = ((c0 + 1) ^ sw) << 4;
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) {
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(at + a_row + i * 32 * C::ROWB + co0);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(at + a_row + i * 32 * C::ROWB + co1);
+          af[t][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(bt + b_row + j * 32 * C::ROWB + co0);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(bt + b_row + j * 32 * C::ROWB + co1);
+          bfr[t][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < C::KSTEPS; ++t)
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[t][i], bfr[t][j], acc[i][j], 0, 0, 0, 127, 0, 127);
+      pipeline_hint<C::KSTEPS, 2 * (C::FM + C::FN), C::FM * C::FN>();
+    }
+  };
+
+  // ---- main loop over a ring of STAGES LDS buffers
+  if (nk > 0) {
+#pragma unroll
+    for (int s = 0; s < C::STAGES - 1; ++s) {
+      fetch(s, k_begin + s * C::BKE);
+      commit(s);
+    }
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    // This wave's DMA loads of slice kt are complete once no more than the
+    // loads of the STAGES-2 later slices are outstanding; its LDS writes (the
+    // register loaders' commits) are complete at lgkmcnt(0). Then one barrier
+    // publishes slice kt to every wave. (A plain __syncthreads would also wait
+    // for the later slices' loads.)
+    if constexpr (DMA_BEHIND == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (DMA_BEHIND == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (DMA_BEHIND == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (DMA_BEHIND == 6) asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (DMA_BEHIND == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (DMA_BEHIND == 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (DMA_BEHIND == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // The buffer of slice kt+STAGES-1 held slice kt-1, which every wave has
+    // finished with (it passed the barrier above). Past the end of K the
+    // loads read zeros, which keeps the number of loads per slice constant.
+    const int nxt = kt + C::STAGES - 1;
+    const int st_next = nxt % C::STAGES;
+    fetch(st_next, k_begin + nxt * C::BKE);
+    compute(kt % C::STAGES);
+    commit(st_next);
+  }
+
+  // The LDS ring becomes the epilogue's staging area: wait until no load into
+  // it is in flight (the trailing zero-block loads included) and every wave is
+  // done reading it.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  float* elds = reinterpret_cast<float*>(smem + wave * EpiLayout<C>::WAVE_BYTES);
+  const int row0 = m0 + wm0, col0 = n0 + wn0;
+  if constexpr (SPLIT) {
+    epilogue<C, OUT_BF16, true, ACT_NONE>(p, acc, elds, row0, col0, lane, split);
+  } else {
+    const int act = p.act;
+    if (act == ACT_NONE)
+      epilogue<C, OUT_BF16, false, ACT_NONE>(p, acc, elds, row0, col0, lane, split);
+    else if (act == ACT_RELU)
+      epilogue<C, OUT_BF16, false, ACT_RELU>(p, acc, elds, row0, col0, lane, split);
+    else if (act == ACT_GELU_ERF)
+      epilogue<C, OUT_BF16, false, ACT_GELU_ERF>(p, acc, elds, row0, col0, lane, split);
+    else
+      epilogue<C, OUT_BF16, false, ACT_GELU_TANH>(p, acc, elds, row0, col0, lane, split);
+  }
+}
+
+// ----------------------------------------------------------- split-K reduction
+
+// C = epilogue(sum over splits s = 0..S-1, in that order, of workspace[s]).
+template <bool FP8, bool OUT_BF16>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs p) {
+  const int64_t MN = static_cast<int64_t>(p.M) * p.N;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= MN) return;
+  const int m = static_cast<int>(idx / p.N);
+  const int n = static_cast<int>(idx - static_cast<int64_t>(m) * p.N);
+  float v = 0.f;
+  for (int s = 0; s < p.split_k; ++s) v += p.workspace[s * MN + idx];
+  if constexpr (FP8) v = v * (p.scale_a[m] * p.scale_b[n]);
+  v = p.alpha * v;
+  const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
+  if (p.beta != 0.f) {
+    const float cin = OUT_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.C)[off])
+                               : static_cast<const float*>(p.C)[off];
+    v += p.beta * cin;
+  }
+  if (p.bias) v += bf16_bits_to_f32(p.bias[n]);
+  v = apply_act(v, p.act);
+  if constexpr (OUT_BF16) static_cast<uint16_t*>(p.C)[off] = f32_to_bf16_bits(v);
+  else static_cast<float*>(p.C)[off] = v;
+}
+
+// ------------------------------------------------------------------- launchers
+#ifndef G355_KERNELS_ONLY
+
+template <class C, int LA, int LB>
+static hipError_t launch_cfg(const Plan& plan, const LaunchSpec& spec, const GemmArgs& a,
+                             hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(plan.grid)), block(C::NT);
+  if (plan.split > 1)
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, false, true>), grid, block, 0, stream, a);
+  else if (spec.out_bf16)
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, true, false>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, false, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+// Tile shapes in use: 128-byte K slices, two LDS stages. (Measured at
+// 4096^3: three or four stages of 64-byte slices were slower.)
+using Big16 = TileCfg<256, 256, 2, 4, false, 128, 2>;
+using Big8 = TileCfg<256, 256, 2, 4, true, 128, 2>;
+using Mid16 = TileCfg<256, 128, 4, 2, false, 128, 2>;
+using Mid8 = TileCfg<256, 128, 4, 2, true, 128, 2>;
+using Small16 = TileCfg<128, 128, 2, 2, false, 128, 2>;
+using Small8 = TileCfg<128, 128, 2, 2, true, 128, 2>;
+
+hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
+                       hipStream_t stream) {
+  GemmArgs a = args;
+  a.a_mn_major = spec.a_kmajor ? 0 : 1;
+  a.b_mn_major = spec.b_kmajor ? 0 : 1;
+  const bool direct = spec.loader_a == LOAD_DIRECT && spec.loader_b == LOAD_DIRECT;
+  if (!direct) {
+    // Register loading runs on the 128x128 tile only.
+    if (spec.fp8) return launch_cfg<Small8, LOAD_GENERIC, LOAD_GENERIC>(plan, spec, a, stream);
+    if (spec.loader_a == LOAD_DIRECT)
+      return launch_cfg<Small16, LOAD_DIRECT, LOAD_GENERIC>(plan, spec, a, stream);
+    if (spec.loader_b == LOAD_DIRECT)
+      return launch_cfg<Small16, LOAD_GENERIC, LOAD_DIRECT>(plan, spec, a, stream);
+    return launch_cfg<Small16, LOAD_GENERIC, LOAD_GENERIC>(plan, spec, a, stream);
+  }
+  if (plan.bm == 256 && plan.bn == 256)
+    return spec.fp8 ? launch_cfg<Big8, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream)
+                    : launch_cfg<Big16, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream);
+  if (plan.bm == 256 && plan.bn == 128)
+    return spec.fp8 ? launch_cfg<Mid8, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream)
+                    : launch_cfg<Mid16, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream);
+  return spec.fp8 ? launch_cfg<Small8, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream)
+                  : launch_cfg<Small16, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream);
+}
+
+hipError_t launch_splitk_reduce(const Plan& plan, const LaunchSpec& spec, const GemmArgs& a,
+                                hipStream_t stream) {
+  (void)plan;
+  const int64_t MN = static_cast<int64_t>(a.M) * a.N;
+  const dim3 grid(static_cast<unsigned>((MN + 255) / 256)), block(256);
+  if (spec.fp8) {
+    if (spec.out_bf16) hipLaunchKernelGGL((splitk_reduce_kernel<true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((splitk_reduce_kernel<true, false>), grid, block, 0, stream, a);
+  } else {
+    if (spec.out_bf16) hipLaunchKernelGGL((splitk_reduce_kernel<false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((splitk_reduce_kernel<false, false>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+#endif  // G355_KERNELS_ONLY
+
+}  // namespace g355

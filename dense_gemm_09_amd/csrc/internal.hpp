@@ -1,0 +1,48 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace g355 {
+
+// How an operand's K slices reach LDS.
+enum Loader : int {
+  LOAD_DIRECT = 0,   // K-major, 16-byte aligned rows: global -> LDS DMA, no registers
+  LOAD_GENERIC = 1,  // any layout / alignment: element loads through registers
+};
+
+enum KernelKind : int { KERNEL_TILE = 0, KERNEL_SKINNY = 1 };
+
+struct Plan {
+  int kernel;        // KernelKind
+  int bm, bn, bk;    // tile (bk in elements)
+  int waves;         // waves per workgroup
+  int split;         // K partitions
+  int k_split_len;   // K elements per partition
+  int64_t grid;      // workgroups of the main kernel
+  size_t workspace;  // bytes
+};
+
+// Chooses the kernel, tile and split for a shape (host arithmetic only).
+Plan make_plan(int64_t M, int64_t N, int64_t K, bool fp8);
+
+struct LaunchSpec {
+  bool fp8;
+  int loader_a, loader_b;  // Loader
+  bool a_kmajor, b_kmajor; // layout of each operand (true = K contiguous)
+  bool out_bf16;
+};
+
+// Enqueue the kernels of a plan. Returns the HIP error of the launch(es).
+hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
+                       hipStream_t stream);
+hipError_t launch_skinny(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
+                         hipStream_t stream);
+hipError_t launch_splitk_reduce(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
+                                hipStream_t stream);
+
+}  // namespace g355

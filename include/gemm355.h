@@ -1,0 +1,140 @@
+/*
+ * gemm355 -- dense GEMM for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ *   C = act( alpha * (scale_a[m] * scale_b[n]) * sum_k A[m,k] B[k,n] + beta * C + bias[n] )
+ *
+ * The operation is the general matrix multiply C = alpha*A*B + beta*C of the
+ * first DeepGEMM page (sec. 1.1: A is MxK, B is KxN, C is MxN), with 16-bit
+ * inputs accumulated in FP32 (same page, sec. 3.1), and the epilogue fused
+ * before the store: bias, then activation, then the output cast (same page,
+ * sec. 6.1). The FP8 entry point takes E4M3 inputs with one FP32 scale per
+ * row of A (per token) and one per column of B (per channel), applied after
+ * accumulation and before the store (DeepGEMM: FP8 precision Tensor Core GEMM
+ * optimisation, sec. 1.2 and 3.2). Like that page's interface (sec. 5.1) the
+ * calls take device pointers, sizes, a scale description, an optional
+ * workspace with a size query, and a stream.
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ * - All matrix, vector and workspace pointers are DEVICE pointers owned by the
+ *   caller. The library never allocates, frees or synchronises, and keeps no
+ *   mutable global state: calls are reentrant and may run on any stream.
+ * - Operand layouts (per operand, gemm_layout):
+ *     A ROW: a(m,k) = A[m*lda + k], lda >= K      A COL: a(m,k) = A[k*lda + m], lda >= M
+ *     B ROW: b(k,n) = B[k*ldb + n], ldb >= N      B COL: b(k,n) = B[n*ldb + k], ldb >= K
+ *   "K-major" means A ROW and B COL. C is always row-major: C[m*ldc + n],
+ *   ldc >= N. C is read (when beta != 0) and written with dtype c_dtype.
+ * - Element types: BF16 (1-8-7, stored as uint16), OCP FP8 E4M3FN (1-4-3,
+ *   bias 7, max 448, stored as uint8), FP32. bias is BF16[N] (NULL for none).
+ *   scale_a is FP32[M] and scale_b FP32[N], contiguous (stride 1).
+ * - Rounding: FP32 accumulation; epilogue arithmetic in FP32; the BF16 output
+ *   cast rounds to nearest even.
+ * - Activations: ReLU max(z,0); GELU_ERF z*Phi(z) = 0.5 z (1 + erf(z/sqrt 2));
+ *   GELU_TANH 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+ * - Quick returns: M == 0 or N == 0 returns GEMM_OK and launches nothing.
+ *   K == 0 gives C = act(beta*C + bias). beta == 0 means C is not read (NaN in
+ *   C is ignored).
+ * - Errors: every argument check happens before anything is enqueued; on a
+ *   non-OK status nothing was launched and no memory was touched. After the
+ *   launch, a HIP launch error is reported as GEMM_ERR_HIP. Faults inside a
+ *   kernel surface at the caller's next synchronisation. Nothing is printed
+ *   and nothing aborts.
+ * - Aliasing: C must not overlap A, B, bias, the scales or the workspace.
+ * - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *   stream) and the call returns without waiting.
+ * - Determinism: for a given (shape, layouts, dtype) the result is bitwise
+ *   reproducible run to run (the split-K reduction sums partials in a fixed
+ *   order; no floating-point atomics).
+ */
+#ifndef GEMM355_H
+#define GEMM355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GEMM_OK = 0,
+  GEMM_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+  GEMM_ERR_BAD_DIM = 2,            /* M, N or K negative, or too large for 32-bit tile indexing */
+  GEMM_ERR_BAD_LD = 3,             /* a leading dimension is smaller than its operand's row extent */
+  GEMM_ERR_BAD_ENUM = 4,           /* unknown layout, output dtype or activation */
+  GEMM_ERR_UNSUPPORTED = 5,        /* a valid combination this library does not implement */
+  GEMM_ERR_WORKSPACE_TOO_SMALL = 6,/* workspace_bytes < gemm_workspace_size(...) */
+  GEMM_ERR_HIP = 7                 /* the HIP runtime rejected the launch */
+} gemm_status;
+
+typedef enum { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout;
+typedef enum { GEMM_OUT_F32 = 0, GEMM_OUT_BF16 = 1 } gemm_out_dtype;
+typedef enum {
+  GEMM_ACT_NONE = 0,
+  GEMM_ACT_RELU = 1,
+  GEMM_ACT_GELU_ERF = 2,
+  GEMM_ACT_GELU_TANH = 3
+} gemm_act;
+
+/*
+ * BF16 x BF16 -> FP32 accumulate -> epilogue -> FP32 or BF16 C.
+ * A: BF16, logical MxK, layout_a / lda as above. B: BF16, logical KxN.
+ * All four layout combinations are accepted.
+ * workspace: device scratch of at least gemm_workspace_size(M, N, K, 0) bytes
+ * (may be NULL when that size is 0). Its contents on entry do not matter.
+ */
+gemm_status gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha,
+                      const void* A, int64_t lda, gemm_layout layout_a,
+                      const void* B, int64_t ldb, gemm_layout layout_b,
+                      float beta, void* C, int64_t ldc, gemm_out_dtype c_dtype,
+                      const void* bias, gemm_act act,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * OCP FP8 E4M3 x E4M3 -> FP32 accumulate -> x scale_a[m]*scale_b[n] -> epilogue.
+ * A must be ROW (K-major, per-token rows) and B COL (K-major, per-channel
+ * rows); other layouts return GEMM_ERR_UNSUPPORTED. scale_a (FP32[M]) and
+ * scale_b (FP32[N]) are required. Codes 0x7F/0xFF (NaN) give undefined results.
+ * workspace: at least gemm_workspace_size(M, N, K, 1) bytes.
+ */
+gemm_status gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, float alpha,
+                            const void* A, int64_t lda, gemm_layout layout_a,
+                            const void* B, int64_t ldb, gemm_layout layout_b,
+                            const float* scale_a, const float* scale_b,
+                            float beta, void* C, int64_t ldc, gemm_out_dtype c_dtype,
+                            const void* bias, gemm_act act,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace a call with these sizes needs (0 when the chosen
+ * kernel needs none). Pure host arithmetic; callable without a GPU. Query
+ * once and allocate up front (the FP8 page's interface, sec. 5.1, separates
+ * the size query from the call for the same reason). is_fp8: 0 for
+ * gemm_bf16, 1 for gemm_fp8_scaled. Negative sizes return 0.
+ */
+size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int is_fp8);
+
+/*
+ * The launch plan the library would use (host arithmetic only, no GPU
+ * needed): tile sizes, split-K factor and grid. Returns GEMM_OK or
+ * GEMM_ERR_BAD_DIM / GEMM_ERR_NULL_POINTER. Intended for tests and tuning.
+ */
+typedef struct {
+  int32_t kernel;       /* 0 = tiled MFMA kernel, 1 = split-K skinny kernel */
+  int32_t tile_m, tile_n, tile_k;
+  int32_t split_k;      /* number of K partitions (1 = none) */
+  int32_t waves;        /* wavefronts per workgroup */
+  int64_t grid;         /* workgroups launched by the main kernel */
+  size_t workspace_bytes;
+} gemm_plan_info;
+
+gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, int is_fp8, gemm_plan_info* out);
+
+/* Static, NUL-terminated name of a status code ("GEMM_OK", ...). */
+const char* gemm_status_string(gemm_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM355_H */

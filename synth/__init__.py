@@ -169,11 +169,11 @@ def make_problem(
     instead of normal samples; for fp8 the scales are then 1.
     """
     if lda is None:
-        lda = K if layout_a == ROW else M
+        lda = max(1, K if layout_a == ROW else M)
     if ldb is None:
-        ldb = N if layout_b == ROW else K
+        ldb = max(1, N if layout_b == ROW else K)
     if ldc is None:
-        ldc = N
+        ldc = max(1, N)
     if int_range is not None:
         a_val = small_ints((M, K), int_range[0], int_range[1], seed_base + 0)
         b_val = small_ints((K, N), int_range[0], int_range[1], seed_base + 1)

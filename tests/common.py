@@ -38,6 +38,7 @@ def compare(p, out, rows=None, cols=None, what=""):
     rn, cn = operand_norms(p, rows, cols)
     what = what or p.name
     if p.c_dtype == 0:
-        return tolerance.check_f32(out, y, rn, cn, p.alpha, what)
+        return tolerance.check_f32(out, y, rn, cn, p.alpha, what,
+                                   frob=1e-5 if p.kind == "bf16" else 1e-4)
     return tolerance.check_bf16(oracle.decode_bf16(out), y, oracle.decode_bf16(ref), rn, cn,
                                 p.alpha, p.act, what)

@@ -1,0 +1,157 @@
+"""C ABI checks that need no GPU: exports, status strings, plans, argument validation.
+
+Every call here fails validation (or returns early) before anything touches
+the HIP runtime, so nothing is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_09_amd as g
+from dense_gemm_09_amd import ACT_GELU_TANH, COL, OUT_BF16, OUT_F32, ROW
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm355.h")
+
+OK, NULLP, BAD_DIM, BAD_LD, BAD_ENUM, UNSUP, WS_SMALL, HIPERR = range(8)
+FAKE = 0x7F0000000000  # a non-NULL address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = g.lib()
+    names = declared_functions()
+    assert set(names) == set(g.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    for code, name in enumerate(g.STATUS):
+        assert g.status_string(code) == name
+    assert g.status_string(99) == "GEMM_ERR_UNKNOWN"
+
+
+def bf16(M=64, N=64, K=64, alpha=1.0, A=FAKE, lda=None, la=ROW, B=FAKE, ldb=None, lb=COL,
+         beta=0.0, C=FAKE, ldc=None, cd=OUT_F32, bias=None, act=0, ws=None, wsb=0):
+    lda = (K if la == ROW else M) if lda is None else lda
+    ldb = (N if lb == ROW else K) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return g.lib().gemm_bf16(M, N, K, alpha, A, lda, la, B, ldb, lb, beta, C, ldc, cd, bias, act,
+                             ws, wsb, None)
+
+
+def fp8(M=64, N=64, K=64, A=FAKE, lda=None, la=ROW, B=FAKE, ldb=None, lb=COL, sa=FAKE, sb=FAKE,
+        C=FAKE, ldc=None, cd=OUT_BF16, ws=None, wsb=0):
+    lda = (K if la == ROW else M) if lda is None else lda
+    ldb = (N if lb == ROW else K) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return g.lib().gemm_fp8_scaled(M, N, K, 1.0, A, lda, la, B, ldb, lb, sa, sb, 0.0, C, ldc, cd,
+                                   None, 0, ws, wsb, None)
+
+
+def test_bad_enums():
+    assert bf16(la=2) == BAD_ENUM
+    assert bf16(lb=-1) == BAD_ENUM
+    assert bf16(cd=2) == BAD_ENUM
+    assert bf16(act=4) == BAD_ENUM
+    assert bf16(act=-1) == BAD_ENUM
+    assert fp8(cd=7) == BAD_ENUM
+
+
+def test_bad_dims():
+    assert bf16(M=-1) == BAD_DIM
+    assert bf16(N=-5) == BAD_DIM
+    assert bf16(K=-1) == BAD_DIM
+    assert bf16(M=(1 << 30) + 1) == BAD_DIM
+    assert fp8(K=-2) == BAD_DIM
+
+
+def test_bad_leading_dimensions():
+    assert bf16(M=8, N=16, K=32, lda=31) == BAD_LD
+    assert bf16(M=8, N=16, K=32, la=COL, lda=7) == BAD_LD
+    assert bf16(M=8, N=16, K=32, lb=ROW, ldb=15) == BAD_LD
+    assert bf16(M=8, N=16, K=32, lb=COL, ldb=31) == BAD_LD
+    assert bf16(M=8, N=16, K=32, ldc=15) == BAD_LD
+    assert bf16(M=8, N=16, K=0, lda=0) == BAD_LD  # ld must be >= 1 even when K == 0
+    assert fp8(M=8, N=16, K=32, lda=16) == BAD_LD
+
+
+def test_fp8_layouts_other_than_k_major_unsupported():
+    assert fp8(la=COL) == UNSUP
+    assert fp8(lb=ROW) == UNSUP
+
+
+def test_null_pointers():
+    assert bf16(C=None) == NULLP
+    assert bf16(A=None) == NULLP
+    assert bf16(B=None) == NULLP
+    assert fp8(sa=None) == NULLP
+    assert fp8(sb=None) == NULLP
+
+
+def test_quick_returns_launch_nothing():
+    # M == 0 or N == 0: OK without touching any pointer
+    assert bf16(M=0, A=None, B=None, C=None) == OK
+    assert bf16(N=0, A=None, B=None, C=None, ldc=1, ldb=64) == OK
+    assert fp8(M=0, A=None, B=None, C=None, sa=None, sb=None) == OK
+
+
+def test_workspace_checked_before_launch():
+    M, N, K = 1, 1024, 8192
+    need = g.workspace_size(M, N, K, False)
+    info = g.plan(M, N, K, False)
+    assert need == info.workspace_bytes
+    if need > 0:
+        assert bf16(M=M, N=N, K=K, ws=None, wsb=0) == NULLP
+        assert bf16(M=M, N=N, K=K, ws=FAKE, wsb=need - 1) == WS_SMALL
+
+
+def test_workspace_size_of_bad_sizes_is_zero():
+    assert g.workspace_size(-1, 5, 5, False) == 0
+    assert g.workspace_size(0, 5, 5, True) == 0
+
+
+@pytest.mark.parametrize("fp8_", [False, True])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (4096, 7168, 2048), (512, 4096, 14336),
+                                   (8192, 14336, 4096), (1, 4096, 4096), (64, 18432, 4096),
+                                   (4093, 4093, 4093), (256, 256, 256), (1, 1, 1), (5, 7, 0)])
+def test_plans_are_consistent(M, N, K, fp8_):
+    p = g.plan(M, N, K, fp8_)
+    assert p.tile_k == (128 if fp8_ else 64)
+    assert p.split_k >= 1
+    assert p.tile_m in (128, 256) and p.tile_n in (128, 256)
+    tiles = -(-M // p.tile_m) * -(-N // p.tile_n)
+    assert p.grid == tiles * p.split_k
+    assert p.workspace_bytes == (p.split_k * M * N * 4 if p.split_k > 1 else 0)
+    assert g.workspace_size(M, N, K, fp8_) == p.workspace_bytes
+    if K == 0:
+        assert p.split_k == 1
+    # every K partition is non-empty
+    if p.split_k > 1:
+        per = -(-K // (p.split_k * p.tile_k)) * p.tile_k
+        assert (p.split_k - 1) * per < K
+
+
+def test_square_4096_uses_one_full_wave_of_256_tiles():
+    p = g.plan(4096, 4096, 4096, False)
+    assert (p.tile_m, p.tile_n, p.split_k, p.grid) == (256, 256, 1, 256)
+
+
+def test_plan_null_out():
+    assert g.lib().gemm_plan(4, 4, 4, 0, None) == NULLP
+
+
+def test_binding_rejects_short_tensors_before_calling():
+    import torch
+    A = torch.zeros(10, dtype=torch.int16)
+    with pytest.raises(ValueError):
+        g._need(A, 1000, "A")  # CPU tensor is rejected as well

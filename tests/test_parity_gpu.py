@@ -1,0 +1,240 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Sizes the oracle finishes in seconds span several tiles and ragged tails;
+the workloads' full sizes are checked on sampled rows (every output element
+depends only on its row of A and column of B, so a row sample is checked
+exactly like a full result). Tolerances: tests/tolerance.py.
+"""
+import numpy as np
+import pytest
+
+import dense_gemm_09_amd as g
+import oracle
+import synth
+from synth import (ACT_GELU_ERF, ACT_GELU_TANH, ACT_NONE, ACT_RELU, COL, OUT_BF16, OUT_F32, ROW,
+                   workloads)
+from tests.common import compare, reference
+from tests.gpu_util import call, run, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_rows(M, n=48, seed=0):
+    """First, last and some random rows (covers the first and the ragged last tile)."""
+    rng = np.random.default_rng(seed)
+    rows = set(range(min(16, M))) | set(range(max(0, M - 16), M))
+    rows |= set(rng.choice(M, size=min(n, M), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+# ------------------------------------------------------------------ small, full compare
+
+def test_small_square_row_major_b():
+    p = workloads.small_square(256)
+    compare(p, run(p))
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 64), (256, 256, 256), (300, 520, 448),
+                                   (257, 129, 192), (1000, 700, 320), (33, 17, 320),
+                                   (1, 1, 8), (513, 1031, 8 * 83)])
+def test_bf16_k_major_shapes(M, N, K):
+    p = synth.make_problem("bf16", M, N, K, seed_base=0x100000 + M + N + K)
+    compare(p, run(p))
+
+
+@pytest.mark.parametrize("la,lb", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)])
+@pytest.mark.parametrize("M,N,K", [(190, 250, 200), (130, 260, 333)])
+def test_bf16_all_layouts(la, lb, M, N, K):
+    p = synth.make_problem("bf16", M, N, K, seed_base=0x200000 + la * 2 + lb + K,
+                           layout_a=la, layout_b=lb)
+    compare(p, run(p))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_padded_leading_dims_with_nan_padding(kind):
+    M, N, K = 200, 300, 256
+    p = synth.make_problem(kind, M, N, K, seed_base=0x300000, lda=K + 16, ldb=K + 32,
+                           ldc=N + 4, c_dtype=OUT_F32)
+    compare(p, run(p))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_unaligned_base_pointers(kind):
+    import torch
+    M, N, K = 150, 140, 256
+    p = synth.make_problem(kind, M, N, K, seed_base=0x310000, c_dtype=OUT_F32)
+    d = to_device(p)
+    esz = 2 if kind == "bf16" else 1
+    # shift A and B by one element inside a larger buffer: rows are no longer 16-byte aligned
+    A2 = torch.zeros(p.A.size + 8, dtype=d["A"].dtype, device="cuda")
+    A2[1:1 + p.A.size] = d["A"].reshape(-1)
+    B2 = torch.zeros(p.B.size + 8, dtype=d["B"].dtype, device="cuda")
+    B2[1:1 + p.B.size] = d["B"].reshape(-1)
+    d["A"], d["B"] = A2.data_ptr() + esz, B2.data_ptr() + esz
+    call(p, d)
+    torch.cuda.synchronize()
+    compare(p, d["C"].cpu().numpy())
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 1024), (131, 77, 640), (64, 4096, 4096)])
+def test_integer_operands_bitwise(kind, M, N, K):
+    lo, hi = (-4, 4) if kind == "bf16" else (-16, 16)
+    p = synth.make_problem(kind, M, N, K, seed_base=0x400000 + M, int_range=(lo, hi),
+                           c_dtype=OUT_F32)
+    _, ref = reference(p)
+    out = run(p)
+    assert np.array_equal(out, ref), np.argwhere(out != ref)[:5]
+
+
+@pytest.mark.parametrize("lb", [ROW, COL])
+def test_identity_and_permutation(lb):
+    M, K = 300, 192
+    p = synth.make_problem("bf16", M, K, K, seed_base=0x500000, layout_b=lb)
+    perm = np.random.default_rng(1).permutation(K)
+    eye = np.zeros((K, K), np.uint16)
+    eye[perm, np.arange(K)] = 0x3F80
+    p.B = synth.store_b(eye, lb, K, 0)
+    p.ldb = K
+    out = run(p)
+    a_vals = oracle.decode_bf16(p.A[:M, :K])
+    assert np.array_equal(out, a_vals[:, perm].astype(np.float32))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+@pytest.mark.parametrize("c_dtype", [OUT_F32, OUT_BF16])
+@pytest.mark.parametrize("act", [ACT_NONE, ACT_RELU, ACT_GELU_ERF, ACT_GELU_TANH])
+def test_epilogue_variants(kind, c_dtype, act):
+    M, N, K = 192, 320, 256
+    p = synth.make_problem(kind, M, N, K, seed_base=0x600000 + act + 4 * c_dtype,
+                           alpha=-1.5, beta=0.75, c_dtype=c_dtype, act=act, bias_std=0.5,
+                           a_std=0.1, b_std=0.1)
+    compare(p, run(p))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_k_zero_is_epilogue_only(kind):
+    M, N = 70, 90
+    p = synth.make_problem(kind, M, N, 0, seed_base=0x700000, beta=2.0, bias_std=1.0,
+                           act=ACT_RELU, c_dtype=OUT_F32)
+    compare(p, run(p))
+
+
+def test_beta_zero_ignores_nan_c():
+    p = synth.make_problem("bf16", 130, 140, 64, seed_base=0x710000, beta=0.0)
+    p.C[:] = np.nan
+    out = run(p)
+    assert np.all(np.isfinite(out))
+    compare(p, out)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+@pytest.mark.parametrize("M,N,K", [(64, 1024, 16384), (8, 512, 8192), (200, 256, 8192)])
+def test_split_k_path(kind, M, N, K):
+    info = g.plan(M, N, K, kind == "fp8")
+    p = synth.make_problem(kind, M, N, K, seed_base=0x800000 + M, beta=0.5, bias_std=0.1,
+                           act=ACT_GELU_ERF, c_dtype=OUT_BF16, a_std=1.0, b_std=0.02)
+    compare(p, run(p))
+    assert info.split_k >= 1
+
+
+def test_split_k_is_exercised():
+    assert any(g.plan(M, N, K, f).split_k > 1 for (M, N, K) in
+               [(64, 1024, 16384), (8, 512, 8192), (200, 256, 8192)] for f in (False, True))
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 64 * 3), (384, 384, 64 * 5), (256, 256, 64 * 7)])
+def test_odd_number_of_k_slices(M, N, K):
+    p = synth.make_problem("bf16", M, N, K, seed_base=0x900000 + K)
+    compare(p, run(p))
+
+
+@pytest.mark.parametrize("kind,M,N,K", [("bf16", 4096, 4096, 4096), ("bf16", 64, 4096, 16384),
+                                        ("fp8", 4096, 7168, 2048), ("fp8", 16, 4096, 8192)])
+def test_deterministic(kind, M, N, K):
+    import torch
+    p = synth.make_problem(kind, M, N, K, seed_base=0xA00000, c_dtype=OUT_F32, beta=0.0)
+    d = to_device(p)
+    call(p, d)
+    torch.cuda.synchronize()
+    first = d["C"].clone()
+    d["C"].fill_(float("nan"))
+    call(p, d)
+    torch.cuda.synchronize()
+    assert torch.equal(first, d["C"])
+
+
+def _e4m3(v):
+    codes = np.arange(256, dtype=np.uint8)
+    return codes[np.where(oracle.decode_e4m3(codes) == v)[0][0]]
+
+
+@pytest.mark.parametrize("q_exp", [-6, -5, -4])
+def test_fp8_mfma_alignment_window(q_exp):
+    """Two products in one FP8 MFMA: 16*16 = 2^8 and 1*2^q. The matrix core keeps
+    bits down to 2^(8-13) = 2^-5 of the larger product's exponent: 2^-6 is
+    dropped, 2^-5 and above are added exactly. The oracle is exact (256 + 2^q).
+    This is the hardware behaviour behind the FP8/FP32-output Frobenius bound."""
+    import torch
+    M, N, K = 1, 1, 64
+    q = 2.0 ** q_exp
+    A = np.zeros((M, K), np.uint8)
+    B = np.zeros((N, K), np.uint8)
+    A[0, 0], B[0, 0] = _e4m3(16.0), _e4m3(16.0)
+    A[0, 1], B[0, 1] = _e4m3(1.0), _e4m3(q)
+    p = synth.make_problem("fp8", M, N, K, seed_base=0xB00000, int_range=(0, 0), c_dtype=OUT_F32)
+    p.A, p.B = A, B
+    _, ref = reference(p)
+    assert float(ref[0, 0]) == 256.0 + q
+    out = run(p)
+    expect = 256.0 if q_exp <= -6 else 256.0 + q
+    assert float(out[0, 0]) == expect, (float(out[0, 0]), expect)
+
+
+# ------------------------------------------------------------------ workloads at full size
+
+def test_square_4096_beta_half():
+    p = workloads.square_bf16(4096)
+    rows = sample_rows(p.M)
+    compare(p, run(p, rows=rows), rows=rows)
+
+
+def test_square_4096_beta_zero():
+    p = workloads.square_bf16(4096)
+    p.beta = 0.0
+    rows = sample_rows(p.M, seed=1)
+    compare(p, run(p, rows=rows), rows=rows)
+
+
+def test_fp8_projection_full_size():
+    p = workloads.fp8_projection()
+    rows = sample_rows(p.M)
+    compare(p, run(p, rows=rows), rows=rows)
+
+
+def test_fp8_square_4096():
+    p = workloads.fp8_projection(4096, 4096, 4096, sub=1)
+    rows = sample_rows(p.M)
+    compare(p, run(p, rows=rows), rows=rows)
+
+
+@pytest.mark.parametrize("M", workloads.FFN_M)
+@pytest.mark.parametrize("N,K", workloads.FFN_SHAPES)
+def test_ffn_projections(M, N, K):
+    p = workloads.ffn(M, N, K)
+    rows = sample_rows(p.M, n=32)
+    compare(p, run(p, rows=rows), rows=rows)
+
+
+@pytest.mark.parametrize("kind,M,N", workloads.all_decode())
+def test_decode_shapes(kind, M, N):
+    p = workloads.decode(kind, M, N)
+    compare(p, run(p))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+@pytest.mark.parametrize("padded", [False, True])
+def test_ragged_4093(kind, padded):
+    p = workloads.ragged(kind, 4093, padded)
+    rows = sample_rows(p.M, n=32)
+    compare(p, run(p, rows=rows), rows=rows)
