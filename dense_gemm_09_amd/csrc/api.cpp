@@ -39,7 +39,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-Plan make_plan(int64_t M, int64_t N, int64_t K, bool fp8) {
+// Tile-kernel plan (any M): tile shape and split from the cost model.
+static Plan make_tile_plan(int64_t M, int64_t N, int64_t K, bool fp8) {
   const int bke = fp8 ? 128 : 64;
   const double flops_per_clk = fp8 ? 8192.0 : 4096.0;  // per CU, dense
   const double clk = 2.4e9;
@@ -79,6 +80,27 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool fp8) {
   }
   if (K == 0) best.k_split_len = bke;
   return best;
+}
+
+// Decode-sized M (<= 16) with K-major, 16-byte aligned operands runs the
+// skinny weight-streaming kernel (16 columns per workgroup, no workspace).
+// The workspace reported is the tile plan's, which the call falls back to
+// when the operands are not eligible.
+constexpr int64_t kSkinnyMaxM = 16;
+
+Plan make_plan(int64_t M, int64_t N, int64_t K, bool fp8) {
+  Plan t = make_tile_plan(M, N, K, fp8);
+  if (M > kSkinnyMaxM) return t;
+  Plan s = t;
+  s.kernel = KERNEL_SKINNY;
+  s.bm = static_cast<int>(16 * ((M + 15) / 16));
+  s.bn = 16;
+  s.bk = fp8 ? 128 : 32;
+  s.waves = 16;
+  s.split = 1;
+  s.k_split_len = static_cast<int>(K);
+  s.grid = (N + 15) / 16;
+  return s;
 }
 
 }  // namespace g355
@@ -139,8 +161,9 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
                                                                             : LOAD_GENERIC;
   if (K == 0) spec.loader_a = spec.loader_b = LOAD_DIRECT;  // nothing is loaded
 
-  Plan p = plan;
-  if (spec.loader_a != LOAD_DIRECT || spec.loader_b != LOAD_DIRECT) {
+  const bool direct = spec.loader_a == LOAD_DIRECT && spec.loader_b == LOAD_DIRECT;
+  Plan p = (plan.kernel == KERNEL_SKINNY && !direct) ? make_tile_plan(M, N, K, fp8) : plan;
+  if (p.kernel == KERNEL_TILE && !direct) {
     p.bm = 128;
     p.bn = 128;
     p.waves = 4;
@@ -171,9 +194,12 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   a.k_split_len = p.k_split_len;
   a.tiles_m = static_cast<int>((M + p.bm - 1) / p.bm);
   a.tiles_n = static_cast<int>((N + p.bn - 1) / p.bn);
-  p.grid = static_cast<int64_t>(a.tiles_m) * a.tiles_n * p.split;
-
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.kernel == KERNEL_SKINNY) {
+    a.a_mn_major = a.b_mn_major = 0;
+    return launch_skinny(p, spec, a, s) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+  }
+  p.grid = static_cast<int64_t>(a.tiles_m) * a.tiles_n * p.split;
   if (launch_tile(p, spec, a, s) != hipSuccess) return GEMM_ERR_HIP;
   if (p.split > 1 && launch_splitk_reduce(p, spec, a, s) != hipSuccess) return GEMM_ERR_HIP;
   return GEMM_OK;

@@ -126,13 +126,18 @@ def test_workspace_size_of_bad_sizes_is_zero():
                                    (4093, 4093, 4093), (256, 256, 256), (1, 1, 1), (5, 7, 0)])
 def test_plans_are_consistent(M, N, K, fp8_):
     p = g.plan(M, N, K, fp8_)
-    assert p.tile_k == (128 if fp8_ else 64)
     assert p.split_k >= 1
+    assert g.workspace_size(M, N, K, fp8_) == p.workspace_bytes
+    if p.kernel == 1:  # skinny: M <= 16, 16 columns per workgroup, no split
+        assert M <= 16 and p.tile_n == 16 and p.split_k == 1
+        assert p.grid == -(-N // 16) and p.tile_m == 16 * -(-M // 16)
+        return
+    assert M > 16
+    assert p.tile_k == (128 if fp8_ else 64)
     assert p.tile_m in (128, 256) and p.tile_n in (128, 256)
     tiles = -(-M // p.tile_m) * -(-N // p.tile_n)
     assert p.grid == tiles * p.split_k
     assert p.workspace_bytes == (p.split_k * M * N * 4 if p.split_k > 1 else 0)
-    assert g.workspace_size(M, N, K, fp8_) == p.workspace_bytes
     if K == 0:
         assert p.split_k == 1
     # every K partition is non-empty

@@ -129,7 +129,7 @@ def test_beta_zero_ignores_nan_c():
 
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8"])
-@pytest.mark.parametrize("M,N,K", [(64, 1024, 16384), (8, 512, 8192), (200, 256, 8192)])
+@pytest.mark.parametrize("M,N,K", [(65, 1024, 16384), (100, 512, 8192), (200, 256, 8192)])
 def test_split_k_path(kind, M, N, K):
     info = g.plan(M, N, K, kind == "fp8")
     p = synth.make_problem(kind, M, N, K, seed_base=0x800000 + M, beta=0.5, bias_std=0.1,
@@ -140,7 +140,28 @@ def test_split_k_path(kind, M, N, K):
 
 def test_split_k_is_exercised():
     assert any(g.plan(M, N, K, f).split_k > 1 for (M, N, K) in
-               [(64, 1024, 16384), (8, 512, 8192), (200, 256, 8192)] for f in (False, True))
+               [(65, 1024, 16384), (100, 512, 8192), (200, 256, 8192)] for f in (False, True))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+@pytest.mark.parametrize("M", [1, 2, 7, 15, 16, 17, 33, 64])
+@pytest.mark.parametrize("N,K", [(40, 256), (1000, 4096), (129, 16 * 37)])
+def test_skinny_kernel(kind, M, N, K):
+    info = g.plan(M, N, K, kind == "fp8")
+    assert info.kernel == (1 if M <= 16 else 0)
+    p = synth.make_problem(kind, M, N, K, seed_base=0x820000 + M + N, beta=0.25, bias_std=0.1,
+                           act=ACT_GELU_TANH, c_dtype=OUT_BF16, a_std=1.0, b_std=0.05)
+    compare(p, run(p))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_skinny_fp32_out_and_fallback(kind):
+    # fp32 output on the skinny kernel, and an unaligned ld that falls back to the tile kernel
+    p = synth.make_problem(kind, 5, 300, 512, seed_base=0x830000, c_dtype=OUT_F32, beta=1.0)
+    compare(p, run(p))
+    q = synth.make_problem(kind, 5, 300, 500, seed_base=0x831000, c_dtype=OUT_F32,
+                           lda=501, ldb=503)
+    compare(q, run(q))
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 512, 64 * 3), (384, 384, 64 * 5), (256, 256, 64 * 7)])
@@ -238,3 +259,33 @@ def test_ragged_4093(kind, padded):
     p = workloads.ragged(kind, 4093, padded)
     rows = sample_rows(p.M, n=32)
     compare(p, run(p, rows=rows), rows=rows)
+
+
+@pytest.mark.parametrize("kind,M,N,K", [("bf16", 4, 4096, 4096), ("fp8", 1, 2048, 4096),
+                                        ("bf16", 300, 520, 448), ("bf16", 100, 512, 8192)])
+def test_graph_replay_matches_eager(kind, M, N, K):
+    """Calls captured in a HIP graph give the eager result on every replay (the
+    library records no memset nodes; split-K uses the caller's workspace)."""
+    import torch
+    p = synth.make_problem(kind, M, N, K, seed_base=0xC00000 + M, beta=0.5, bias_std=0.1,
+                           act=ACT_GELU_ERF, c_dtype=OUT_BF16)
+    d = to_device(p)
+    c0 = d["C"].clone()
+    need = g.workspace_size(M, N, K, kind == "fp8")
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    call(p, d, workspace=ws)
+    torch.cuda.synchronize()
+    eager = d["C"].clone()
+    compare(p, eager.cpu().numpy().view(np.uint16)[:, :N])
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    d["C"].copy_(c0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        call(p, d, workspace=ws, stream=s)
+    for _ in range(3):
+        d["C"].copy_(c0)           # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d["C"], eager)
