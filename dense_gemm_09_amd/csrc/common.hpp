@@ -54,12 +54,37 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 
 // ---------------------------------------------------------------- epilogue math
 
+// e^x from the hardware base-2 exponential (v_exp_f32).
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: for x >= 0, erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5)
+// e^(-x^2) with t = 1 / (1 + p x), |error| <= 1.5e-7; odd symmetry for x < 0.
+// About a dozen VALU operations (one hardware exp, one hardware reciprocal)
+// instead of a full-precision library erf.
+__device__ __forceinline__ float erf_as7126(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.f + 0.3275911f * ax);
+  float poly = 1.061405429f;
+  poly = poly * t - 1.453152027f;
+  poly = poly * t + 1.421413741f;
+  poly = poly * t - 0.284496736f;
+  poly = poly * t + 0.254829592f;
+  poly = poly * t;
+  const float r = 1.f - poly * fast_exp(-ax * ax);
+  return copysignf(r, x);
+}
+
 __device__ __forceinline__ float apply_act(float z, int act) {
   if (act == ACT_RELU) return z > 0.f ? z : 0.f;
-  if (act == ACT_GELU_ERF) return 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
+  if (act == ACT_GELU_ERF) return 0.5f * z * (1.f + erf_as7126(z * 0.70710678118654752f));
   if (act == ACT_GELU_TANH) {
-    const float c = 0.79788456080286536f;  // sqrt(2/pi)
-    return 0.5f * z * (1.f + tanhf(c * (z + 0.044715f * z * z * z)));
+    // tanh(u) = 1 - 2 / (1 + e^(2u)); saturates correctly for large |u|.
+    const float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);  // sqrt(2/pi) (...)
+    const float th = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + fast_exp(2.f * u));
+    return 0.5f * z * (1.f + th);
   }
   return z;
 }

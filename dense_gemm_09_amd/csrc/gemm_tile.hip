@@ -81,11 +81,14 @@ struct TileCfg {
 template <class C, int ROWS>
 struct DirectLoader {
   static constexpr int IPW = ROWS / C::RPS / C::NWAVES;  // 1 KB segments per wave per slice
-  const char* src[IPW];                                 // row start + chunk offset (k excluded)
-  int kc[IPW];                                          // first K element of the lane's chunk
+  // Byte offset of this lane's chunk (row start + chunk, k excluded) from the
+  // operand base. Offsets are 32-bit (operands under 4 GiB, checked on the
+  // host), so a load is the wave-uniform base (SGPRs) plus one VGPR: the
+  // per-slice advance is a scalar add.
+  uint32_t off[IPW];
+  int kc[IPW];  // first K element of the lane's chunk
 
-  __device__ __forceinline__ void init(const void* base, int64_t ld, int row0, int rows, int wave,
-                                       int lane) {
+  __device__ __forceinline__ void init(int64_t ld, int row0, int rows, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int s = wave * IPW + i;
@@ -93,19 +96,31 @@ struct DirectLoader {
       const int c = (lane % C::CPR) ^ swz<C::CPR>(r);
       int g = row0 + r;
       g = g < rows ? g : rows - 1;
-      src[i] = static_cast<const char*>(base) + (static_cast<int64_t>(g) * ld) * C::ES + c * 16;
+      off[i] = static_cast<uint32_t>(static_cast<int64_t>(g) * ld * C::ES) + c * 16;
       kc[i] = c * C::CE;
     }
   }
 
-  __device__ __forceinline__ void issue(char* lds_tile, int wave, int k0, int k_end) const {
+  // base: operand pointer advanced to element k0 (wave-uniform). full: the
+  // whole slice lies below k_end (wave-uniform), so no lane needs a bound check.
+  __device__ __forceinline__ void issue(char* lds_tile, int wave, const char* base, int k0,
+                                        int k_end, bool full) const {
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int s = wave * IPW + i;
-      const char* g = (k0 + kc[i] < k_end) ? src[i] + static_cast<int64_t>(k0) * C::ES
-                                           : reinterpret_cast<const char*>(g_zero16);
-      __builtin_amdgcn_global_load_lds((const G355_GLOBAL void*)(g),
-                                       (G355_LDS void*)(lds_tile + s * 1024), 16, 0, 0);
+      for (int i = 0; i < IPW; ++i) {
+        const int s = wave * IPW + i;
+        __builtin_amdgcn_global_load_lds((const G355_GLOBAL void*)(base + off[i]),
+                                         (G355_LDS void*)(lds_tile + s * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int s = wave * IPW + i;
+        const char* g = (k0 + kc[i] < k_end) ? base + off[i]
+                                             : reinterpret_cast<const char*>(g_zero16);
+        __builtin_amdgcn_global_load_lds((const G355_GLOBAL void*)(g),
+                                         (G355_LDS void*)(lds_tile + s * 1024), 16, 0, 0);
+      }
     }
   }
 };
@@ -235,44 +250,47 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
     }
   }
 
+  // C_in of strip i+1 is requested before strip i is processed, so its HBM
+  // latency overlaps the epilogue math and stores of strip i.
+  float4 cin[2][E::ITERS];
+  auto load_cin = [&](int i, float4 (&dst)[E::ITERS]) {
+#pragma unroll
+    for (int it = 0; it < E::ITERS; ++it) {
+      const int m = row0 + 32 * i + it * E::RPI + rq;
+      dst[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (m >= M) continue;
+      const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
+      if (vec_ok) {
+        if constexpr (OUT_BF16) {
+          const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.C) + off);
+          dst[it] = make_float4(__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xffff0000u),
+                                __uint_as_float(h.y << 16), __uint_as_float(h.y & 0xffff0000u));
+        } else {
+          dst[it] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.C) + off);
+        }
+      } else {
+        float t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (n + q < N)
+            t[q] = OUT_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.C)[off + q])
+                            : static_cast<const float*>(p.C)[off + q];
+        dst[it] = make_float4(t[0], t[1], t[2], t[3]);
+      }
+    }
+  };
+  const bool use_c = !SPLIT && p.beta != 0.f;
+  if (use_c) load_cin(0, cin[0]);
+
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
+    if (use_c && i + 1 < C::FM) load_cin(i + 1, cin[(i + 1) & 1]);
     // accumulators of rows 32i..32i+31 -> LDS strip
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         lds[(8 * (e >> 2) + 4 * half + (e & 3)) * E::STR + 32 * j + (lane & 31)] = acc[i][j][e];
-
-    float4 cin[E::ITERS];
-    if constexpr (!SPLIT) {
-      if (p.beta != 0.f) {
-#pragma unroll
-        for (int it = 0; it < E::ITERS; ++it) {
-          const int m = row0 + 32 * i + it * E::RPI + rq;
-          cin[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (m >= M) continue;
-          const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
-          if (vec_ok) {
-            if constexpr (OUT_BF16) {
-              const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.C) + off);
-              cin[it] = make_float4(__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xffff0000u),
-                                    __uint_as_float(h.y << 16), __uint_as_float(h.y & 0xffff0000u));
-            } else {
-              cin[it] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.C) + off);
-            }
-          } else {
-            float t[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (n + q < N)
-                t[q] = OUT_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.C)[off + q])
-                                : static_cast<const float*>(p.C)[off + q];
-            cin[it] = make_float4(t[0], t[1], t[2], t[3]);
-          }
-        }
-      }
-    }
 
 #pragma unroll
     for (int it = 0; it < E::ITERS; ++it) {
@@ -293,7 +311,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
         continue;
       } else {
         const float sa = C::FP8 ? p.scale_a[m] : 1.f;
-        const float c4[4] = {cin[it].x, cin[it].y, cin[it].z, cin[it].w};
+        const float4 cc = cin[i & 1][it];
+        const float c4[4] = {cc.x, cc.y, cc.z, cc.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float z = v[q];
@@ -342,7 +361,7 @@ gemm_tile_kernel(GemmArgs p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // ---- which tile and which K range
   const int tiles = p.tiles_m * p.tiles_n;
@@ -361,28 +380,35 @@ gemm_tile_kernel(GemmArgs p) {
   GenericLoader<C, C::BM> ga;
   GenericLoader<C, C::BN> gb;
   if constexpr (LA == LOAD_DIRECT) {
-    da.init(p.A, p.lda, m0, p.M, wave, lane);
+    da.init(p.lda, m0, p.M, wave, lane);
   } else {
     ga.base = static_cast<const char*>(p.A); ga.ld = p.lda; ga.row0 = m0; ga.rows = p.M;
     ga.kmajor = p.a_mn_major == 0;
   }
   if constexpr (LB == LOAD_DIRECT) {
-    db.init(p.B, p.ldb, n0, p.N, wave, lane);
+    db.init(p.ldb, n0, p.N, wave, lane);
   } else {
     gb.base = static_cast<const char*>(p.B); gb.ld = p.ldb; gb.row0 = n0; gb.rows = p.N;
     gb.kmajor = p.b_mn_major == 0;
   }
   constexpr int DMA_PER_SLICE = (LA == LOAD_DIRECT ? DirectLoader<C, C::BM>::IPW : 0) +
                                 (LB == LOAD_DIRECT ? DirectLoader<C, C::BN>::IPW : 0);
+  // Loads behind slice kt's stage loads at the wait: those of the STAGES-2
+  // later slices.
   constexpr int DMA_BEHIND = DMA_PER_SLICE * (C::STAGES - 2);
 
   auto a_tile = [&](int st) { return smem + st * C::STAGE; };
   auto b_tile = [&](int st) { return smem + st * C::STAGE + C::A_BYTES; };
 
   auto fetch = [&](int st, int k0) {
-    if constexpr (LA == LOAD_DIRECT) da.issue(a_tile(st), wave, k0, k_end);
+    const bool full = k0 + C::BKE <= k_end;
+    if constexpr (LA == LOAD_DIRECT)
+      da.issue(a_tile(st), wave, static_cast<const char*>(p.A) + static_cast<int64_t>(k0) * C::ES,
+               k0, k_end, full);
     else ga.load(tid, k0, k_end);
-    if constexpr (LB == LOAD_DIRECT) db.issue(b_tile(st), wave, k0, k_end);
+    if constexpr (LB == LOAD_DIRECT)
+      db.issue(b_tile(st), wave, static_cast<const char*>(p.B) + static_cast<int64_t>(k0) * C::ES,
+               k0, k_end, full);
     else gb.load(tid, k0, k_end);
   };
   auto commit = [&](int st) {
