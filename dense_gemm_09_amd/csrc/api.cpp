@@ -155,14 +155,16 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   spec.b_kmajor = layout_b == GEMM_COL_MAJOR;
   spec.out_bf16 = c_dtype == GEMM_OUT_BF16;
   const bool k_ok = K % ce == 0;
-  // The DMA loader addresses an operand with 32-bit byte offsets from its base.
+  // The DMA loader addresses an operand with 32-bit byte offsets from its base
+  // and marks chunks past K with an offset just beyond the operand's extent:
+  // the extent must stay under 2 GiB.
   const int64_t es = fp8 ? 1 : 2;
-  const auto under4g = [&](int64_t rows, int64_t ld) {
-    return ((rows - 1) * ld + K) * es < (int64_t{1} << 32);
+  const auto under2g = [&](int64_t rows, int64_t ld) {
+    return ((rows - 1) * ld + K) * es < (int64_t{1} << 31);
   };
-  spec.loader_a = (spec.a_kmajor && k_ok && lda % ce == 0 && aligned16(A) && under4g(M, lda))
+  spec.loader_a = (spec.a_kmajor && k_ok && lda % ce == 0 && aligned16(A) && under2g(M, lda))
                       ? LOAD_DIRECT : LOAD_GENERIC;
-  spec.loader_b = (spec.b_kmajor && k_ok && ldb % ce == 0 && aligned16(B) && under4g(N, ldb))
+  spec.loader_b = (spec.b_kmajor && k_ok && ldb % ce == 0 && aligned16(B) && under2g(N, ldb))
                       ? LOAD_DIRECT : LOAD_GENERIC;
   if (K == 0) spec.loader_a = spec.loader_b = LOAD_DIRECT;  // nothing is loaded
 

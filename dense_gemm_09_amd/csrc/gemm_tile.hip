@@ -38,6 +38,10 @@
 
 namespace g355 {
 
+// Word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data format,
+// no swizzle, no index stride).
+constexpr int kBufferWord3 = 0x00020000;
+
 // A 16-byte block of zeros in global memory, read by loads whose chunk lies
 // at or past the end of K.
 __device__ __attribute__((aligned(16))) uint32_t g_zero16[4] = {0u, 0u, 0u, 0u};
@@ -49,9 +53,11 @@ __device__ __forceinline__ int swz(int r) {
   else return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
-template <int BM_, int BN_, int WM_, int WN_, bool FP8_, int ROWB_, int STAGES_>
+template <int BM_, int BN_, int WM_, int WN_, bool FP8_, int ROWB_, int STAGES_, int SPREAD_ = 1>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, ROWB = ROWB_, STAGES = STAGES_;
+  // K-steps over which the global->LDS loads of one slice are issued.
+  static constexpr int SPREAD = SPREAD_;
   static constexpr bool FP8 = FP8_;
   static constexpr int NWAVES = WM * WN;
   static constexpr int NT = NWAVES * 64;
@@ -74,19 +80,24 @@ struct TileCfg {
   static_assert((BM / RPS) % NWAVES == 0 && (BN / RPS) % NWAVES == 0, "DMA segments per wave");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(STAGES >= 2 && STAGES * STAGE <= 160 * 1024, "LDS budget");
+  static_assert(SPREAD >= 1 && SPREAD <= KSTEPS, "load spread");
 };
 
 // ------------------------------------------------------------------ DMA loader
 
-template <class C, int ROWS>
+template <class C, int ROWS, int NW = C::NWAVES>
 struct DirectLoader {
-  static constexpr int IPW = ROWS / C::RPS / C::NWAVES;  // 1 KB segments per wave per slice
+  // NW waves issue the loads of a tile; each issues IPW 1 KB segments per slice.
+  static constexpr int IPW = ROWS / C::RPS / NW;
   // Byte offset of this lane's chunk (row start + chunk, k excluded) from the
   // operand base. Offsets are 32-bit (operands under 4 GiB, checked on the
   // host), so a load is the wave-uniform base (SGPRs) plus one VGPR: the
   // per-slice advance is a scalar add.
   uint32_t off[IPW];
-  int kc[IPW];  // first K element of the lane's chunk
+  // First K element of the lane's chunk in segments of even and of odd index:
+  // a segment holds RPS consecutive rows starting at a multiple of RPS, so the
+  // swizzle of a lane's row depends on the segment only through its parity.
+  int kc2[2];
 
   __device__ __forceinline__ void init(int64_t ld, int row0, int rows, int wave, int lane) {
 #pragma unroll
@@ -97,26 +108,49 @@ struct DirectLoader {
       int g = row0 + r;
       g = g < rows ? g : rows - 1;
       off[i] = static_cast<uint32_t>(static_cast<int64_t>(g) * ld * C::ES) + c * 16;
-      kc[i] = c * C::CE;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = C::RPS * q + lane / C::CPR;
+      kc2[q] = ((lane % C::CPR) ^ swz<C::CPR>(r)) * C::CE;
+    }
+  }
+
+  // Loads of a slice as buffer loads: the operand's descriptor (whose range
+  // is the operand's extent), this lane's 32-bit offset and the slice's
+  // wave-uniform byte offset koff = k0 * ES. Lanes whose chunk starts at or
+  // past k_end use the offset `oob` (the extent): the buffer's range check
+  // turns their load into zeros. full: no lane of the slice is past k_end.
+  template <int I0 = 0, int I1 = IPW>
+  __device__ __forceinline__ void issue_buf(char* lds_tile, int wave, __amdgpu_buffer_rsrc_t rsrc,
+                                            int koff, uint32_t oob, int k0, int k_end,
+                                            bool full) const {
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+      const int s = wave * IPW + i;
+      const uint32_t vo = (full || k0 + kc2[s & 1] < k_end) ? off[i] : oob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (G355_LDS void*)(lds_tile + s * 1024), 16,
+                                               static_cast<int>(vo), koff, 0, 0);
     }
   }
 
   // base: operand pointer advanced to element k0 (wave-uniform). full: the
   // whole slice lies below k_end (wave-uniform), so no lane needs a bound check.
+  template <int I0 = 0, int I1 = IPW>
   __device__ __forceinline__ void issue(char* lds_tile, int wave, const char* base, int k0,
                                         int k_end, bool full) const {
     if (full) {
 #pragma unroll
-      for (int i = 0; i < IPW; ++i) {
+      for (int i = I0; i < I1; ++i) {
         const int s = wave * IPW + i;
         __builtin_amdgcn_global_load_lds((const G355_GLOBAL void*)(base + off[i]),
                                          (G355_LDS void*)(lds_tile + s * 1024), 16, 0, 0);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < IPW; ++i) {
+      for (int i = I0; i < I1; ++i) {
         const int s = wave * IPW + i;
-        const char* g = (k0 + kc[i] < k_end) ? base + off[i]
+        const char* g = (k0 + kc2[s & 1] < k_end) ? base + off[i]
                                              : reinterpret_cast<const char*>(g_zero16);
         __builtin_amdgcn_global_load_lds((const G355_GLOBAL void*)(g),
                                          (G355_LDS void*)(lds_tile + s * 1024), 16, 0, 0);
@@ -182,28 +216,79 @@ struct GenericLoader {
 
 // ------------------------------------------------------------ MFMA schedule
 
-// Instruction order for one slice: the first k-step's fragment reads, then
-// each k-step's MFMAs interleaved one-for-one with the next k-step's reads, so
-// the LDS latency of a k-step hides behind the previous k-step's MFMAs.
-// (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read.)
-template <int KSTEPS, int READS, int MFMAS>
-__device__ __forceinline__ void pipeline_hint() {
-  __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+template <bool FP8> struct FragOf { using type = bf16x8; };   // 8 BF16: one ds_read_b128
+template <> struct FragOf<true> { using type = i32x8; };     // 32 FP8: two ds_read_b128
+
+// Wait until at most N of this wave's global loads are outstanding and all of
+// its LDS operations are done, then barrier. (N is the number of loads of
+// later slices that may stay in flight; loads complete in issue order.)
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Instruction order inside one k-step (sched_group_barrier masks: 0x008
+// MFMA, 0x010 VMEM, 0x100 LDS read): each of the first R/2 MFMAs is followed
+// by two fragment reads of the next k-step, so all reads are out early and
+// their latency hides behind the remaining MFMAs; then the V global->LDS
+// loads are spread over the MFMAs that follow.
+template <int R, int M, int V>
+__device__ __forceinline__ void step_hint() {
+  constexpr int R2 = (R + 1) / 2;
+  static_assert(R2 <= M, "reads per MFMA");
 #pragma unroll
-  for (int t = 0; t < KSTEPS; ++t) {
-    if (t + 1 < KSTEPS) {
+  for (int q = 0; q < R / 2; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  if constexpr (R % 2 == 1) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  constexpr int REST = M - R2;
+  if constexpr (V == 0) {
+    if constexpr (REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);
+  } else if constexpr (REST == 0) {
+    __builtin_amdgcn_sched_group_barrier(0x010, V, 0);
+  } else {
+    constexpr int PER = (V + REST - 1) / REST;  // loads after each remaining MFMA
+    constexpr int FULL = V / PER, LAST = V % PER;
 #pragma unroll
-      for (int q = 0; q < (READS < MFMAS ? READS : MFMAS); ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      if constexpr (READS < MFMAS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - READS, 0);
-      else if constexpr (READS > MFMAS) __builtin_amdgcn_sched_group_barrier(0x100, READS - MFMAS, 0);
-    } else {
-      __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, 0);
+    for (int q = 0; q < FULL; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, PER, 0);
     }
+    if constexpr (LAST > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x010, LAST, 0);
+    }
+    constexpr int TAIL = REST - FULL - (LAST > 0 ? 1 : 0);
+    if constexpr (TAIL > 0) __builtin_amdgcn_sched_group_barrier(0x008, TAIL, 0);
   }
 }
+
+// Part P (of SPREAD) of one wave's global->LDS loads of a slice: the A loads
+// followed by the B loads, cut into SPREAD consecutive runs.
+template <class C, int NA, int NB, int P>
+struct DmaPart {
+  static constexpr int T = NA + NB;
+  static constexpr int LO = P * T / C::SPREAD, HI = (P + 1) * T / C::SPREAD;
+  static constexpr int A0 = LO < NA ? LO : NA, A1 = HI < NA ? HI : NA;
+  static constexpr int B0 = LO > NA ? LO - NA : 0, B1 = HI > NA ? HI - NA : 0;
+  static constexpr int COUNT = P < C::SPREAD ? HI - LO : 0;
+  template <class DA, class DB>
+  __device__ __forceinline__ static void issue(const DA& da, const DB& db, char* at, char* bt,
+                                               int wave, __amdgpu_buffer_rsrc_t ra,
+                                               __amdgpu_buffer_rsrc_t rb, uint32_t oob_a,
+                                               uint32_t oob_b, int koff, int k0, int k_end,
+                                               bool full) {
+    if constexpr (P < C::SPREAD && A1 > A0)
+      da.template issue_buf<A0, A1>(at, wave, ra, koff, oob_a, k0, k_end, full);
+    if constexpr (P < C::SPREAD && B1 > B0)
+      db.template issue_buf<B0, B1>(bt, wave, rb, koff, oob_b, k0, k_end, full);
+  }
+};
 
 // ------------------------------------------------------------------ epilogue
 
@@ -347,6 +432,25 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
   }
 }
 
+// Runs the epilogue with the activation as a compile-time parameter.
+template <class C, bool OUT_BF16, bool SPLIT>
+__device__ __forceinline__ void run_epilogue(const GemmArgs& p, const f32x16 (&acc)[C::FM][C::FN],
+                                             float* lds, int row0, int col0, int lane, int split) {
+  if constexpr (SPLIT) {
+    epilogue<C, OUT_BF16, true, ACT_NONE>(p, acc, lds, row0, col0, lane, split);
+  } else {
+    const int act = p.act;
+    if (act == ACT_NONE)
+      epilogue<C, OUT_BF16, false, ACT_NONE>(p, acc, lds, row0, col0, lane, split);
+    else if (act == ACT_RELU)
+      epilogue<C, OUT_BF16, false, ACT_RELU>(p, acc, lds, row0, col0, lane, split);
+    else if (act == ACT_GELU_ERF)
+      epilogue<C, OUT_BF16, false, ACT_GELU_ERF>(p, acc, lds, row0, col0, lane, split);
+    else
+      epilogue<C, OUT_BF16, false, ACT_GELU_TANH>(p, acc, lds, row0, col0, lane, split);
+  }
+}
+
 // ------------------------------------------------------------------- the kernel
 
 template <class C, int LA, int LB, bool OUT_BF16, bool SPLIT>
@@ -393,14 +497,15 @@ gemm_tile_kernel(GemmArgs p) {
   }
   constexpr int DMA_PER_SLICE = (LA == LOAD_DIRECT ? DirectLoader<C, C::BM>::IPW : 0) +
                                 (LB == LOAD_DIRECT ? DirectLoader<C, C::BN>::IPW : 0);
-  // Loads behind slice kt's stage loads at the wait: those of the STAGES-2
-  // later slices.
+  // At boundary j the loads of slice j+1 must be complete; those of slices
+  // j+2 .. j+STAGES-1 (issued at the STAGES-2 boundaries before) may still
+  // be in flight. Register-loaded slices are already in LDS by then.
   constexpr int DMA_BEHIND = DMA_PER_SLICE * (C::STAGES - 2);
 
   auto a_tile = [&](int st) { return smem + st * C::STAGE; };
   auto b_tile = [&](int st) { return smem + st * C::STAGE + C::A_BYTES; };
 
-  auto fetch = [&](int st, int k0) {
+  auto fetch = [&](int st, int k0) __attribute__((always_inline)) {
     const bool full = k0 + C::BKE <= k_end;
     if constexpr (LA == LOAD_DIRECT)
       da.issue(a_tile(st), wave, static_cast<const char*>(p.A) + static_cast<int64_t>(k0) * C::ES,
@@ -411,7 +516,7 @@ gemm_tile_kernel(GemmArgs p) {
                k0, k_end, full);
     else gb.load(tid, k0, k_end);
   };
-  auto commit = [&](int st) {
+  auto commit = [&](int st) __attribute__((always_inline)) {
     if constexpr (LA != LOAD_DIRECT) ga.store(a_tile(st), tid);
     if constexpr (LB != LOAD_DIRECT) gb.store(b_tile(st), tid);
   };
@@ -432,94 +537,149 @@ gemm_tile_kernel(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // All fragment reads of a slice are issued first, then its MFMAs: the LDS
-  // latency of later k-steps hides behind the MFMAs of earlier ones.
-  auto compute = [&](int st) {
+  // Fragment registers: two sets, so that the reads of the next k-step go to
+  // one set while the MFMAs of the current k-step consume the other.
+  using Frag = typename FragOf<C::FP8>::type;
+  Frag fa0[C::FM], fb0[C::FN], fa1[C::FM], fb1[C::FN];
+
+  // LDS -> registers: the fragments of k-step t of the slice in stage st.
+  auto reads = [&](int st, int t, Frag (&fa)[C::FM], Frag (&fb)[C::FN]) {
     const char* at = a_tile(st);
     const char* bt = b_tile(st);
     if constexpr (!C::FP8) {
-      bf16x8 af[C::KSTEPS][C::FM], bfr[C::KSTEPS][C::FN];
+      const int co = ((2 * t + half) ^ sw) << 4;
 #pragma unroll
-      for (int t = 0; t < C::KSTEPS; ++t) {
-        const int co = ((2 * t + half) ^ sw) << 4;
+      for (int i = 0; i < C::FM; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8*>(at + a_row + i * 32 * C::ROWB + co);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-          af[t][i] = *reinterpret_cast<const bf16x8*>(at + a_row + i * 32 * C::ROWB + co);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          bfr[t][j] = *reinterpret_cast<const bf16x8*>(bt + b_row + j * 32 * C::ROWB + co);
-      }
-#pragma unroll
-      for (int t = 0; t < C::KSTEPS; ++t)
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t][i], bfr[t][j], acc[i][j],
-                                                                0, 0, 0);
-      pipeline_hint<C::KSTEPS, C::FM + C::FN, C::FM * C::FN>();
+      for (int j = 0; j < C::FN; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8*>(bt + b_row + j * 32 * C::ROWB + co);
     } else {
-      i32x8 af[C::KSTEPS][C::FM], bfr[C::KSTEPS][C::FN];
+      const int c0 = 4 * t + 2 * half;
+      const int co0 = (c0 ^ sw) << 4;
+      const int co1 = ((c0 + 1) ^ sw) << 4;
 #pragma unroll
-      for (int t = 0; t < C::KSTEPS; ++t) {
-        const int c0 = 4 * t + 2 * half;
-        const int co0 = (c0 ^ sw) << 4;
-        const int co1 = ((c0 + 1) ^ sw) << 4;
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(at + a_row + i * 32 * C::ROWB + co0);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(at + a_row + i * 32 * C::ROWB + co1);
-          af[t][i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(bt + b_row + j * 32 * C::ROWB + co0);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(bt + b_row + j * 32 * C::ROWB + co1);
-          bfr[t][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+      for (int i = 0; i < C::FM; ++i) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(at + a_row + i * 32 * C::ROWB + co0);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(at + a_row + i * 32 * C::ROWB + co1);
+        fa[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
 #pragma unroll
-      for (int t = 0; t < C::KSTEPS; ++t)
+      for (int j = 0; j < C::FN; ++j) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(bt + b_row + j * 32 * C::ROWB + co0);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(bt + b_row + j * 32 * C::ROWB + co1);
+        fb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    }
+  };
+  auto mfmas = [&](const Frag (&fa)[C::FM], const Frag (&fb)[C::FN]) {
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-          for (int j = 0; j < C::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[t][i], bfr[t][j], acc[i][j], 0, 0, 0, 127, 0, 127);
-      pipeline_hint<C::KSTEPS, 2 * (C::FM + C::FN), C::FM * C::FN>();
+      for (int j = 0; j < C::FN; ++j) {
+        if constexpr (C::FP8)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0,
+                                                                     0, 0, 127, 0, 127);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+  };
+
+  // The K loop is one stream of k-steps. Each k-step issues its MFMAs on the
+  // fragment set read during the previous k-step, interleaved with the reads
+  // of the next k-step into the other set. Where the next k-step opens slice
+  // j+1 ("boundary j"), the wave first waits for its share of that slice's
+  // loads and for its own LDS traffic, and one barrier then publishes slice
+  // j+1 and certifies that every wave has finished reading slice j; the loads
+  // of slice j+STAGES then go into slice j's buffer. So the MFMAs of a
+  // slice's last k-step overlap the barrier's aftermath and the first reads
+  // of the next slice, and a slice's loads have STAGES-1 slices of MFMA work
+  // to arrive. Register-loaded operands hold the slice fetched at boundary j
+  // in registers and write it to LDS just before boundary j+1.
+  constexpr int READS = C::FP8 ? 2 * (C::FM + C::FN) : C::FM + C::FN;
+  constexpr int MFMAS = C::FM * C::FN;
+  constexpr bool ALL_DMA = LA == LOAD_DIRECT && LB == LOAD_DIRECT;
+  // With both operands on the DMA path, the loads of slice s are issued in
+  // SPREAD parts: part 0 at boundary s-STAGES, part p in the (p-1)-th k-step
+  // after it, so that the loads of all waves do not queue up at once.
+  constexpr int NA = LA == LOAD_DIRECT ? DirectLoader<C, C::BM>::IPW : 0;
+  constexpr int NB = LB == LOAD_DIRECT ? DirectLoader<C, C::BN>::IPW : 0;
+  using Part0 = DmaPart<C, NA, NB, 0>;
+  using Part1 = DmaPart<C, NA, NB, 1>;
+  using Part2 = DmaPart<C, NA, NB, 2>;
+  using Part3 = DmaPart<C, NA, NB, 3>;
+  // Buffer descriptors over each operand's extent (under 2 GiB, checked on
+  // the host, so an offset past the extent plus the slice offset cannot wrap
+  // into range).
+  const uint32_t ext_a = static_cast<uint32_t>(
+      (static_cast<int64_t>(p.M - 1) * p.lda + p.K) * C::ES);
+  const uint32_t ext_b = static_cast<uint32_t>(
+      (static_cast<int64_t>(p.N - 1) * p.ldb + p.K) * C::ES);
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.A), 0, static_cast<int>(ext_a), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.B), 0, static_cast<int>(ext_b), kBufferWord3);
+  auto dma_part = [&](auto part, int s) {
+    using Pt = decltype(part);
+    const int k0 = k_begin + s * C::BKE;
+    const int st = s % C::STAGES;
+    Pt::issue(da, db, a_tile(st), b_tile(st), wave, rsrc_a, rsrc_b, ext_a, ext_b, k0 * C::ES, k0,
+              k_end, k0 + C::BKE <= k_end);
+  };
+  auto boundary = [&](int j) {
+    commit((j + C::STAGES - 1) % C::STAGES);
+    wait_loads_and_barrier<DMA_BEHIND>();
+    if constexpr (ALL_DMA) dma_part(Part0{}, j + C::STAGES);
+    else fetch(j % C::STAGES, k_begin + (j + C::STAGES) * C::BKE);
+  };
+  auto step = [&](int j, int t, const Frag (&ca)[C::FM], const Frag (&cb)[C::FN],
+                  Frag (&na)[C::FM], Frag (&nb)[C::FN]) {
+    if (t == C::KSTEPS - 1) {
+      boundary(j);
+      reads((j + 1) % C::STAGES, 0, na, nb);
+      mfmas(ca, cb);
+      step_hint<READS, MFMAS, ALL_DMA ? Part0::COUNT : 0>();
+    } else {
+      // Later parts of the loads of slice j-1+STAGES.
+      if constexpr (ALL_DMA) {
+        if (t == 0) dma_part(Part1{}, j - 1 + C::STAGES);
+        if (t == 1) dma_part(Part2{}, j - 1 + C::STAGES);
+        if (t == 2) dma_part(Part3{}, j - 1 + C::STAGES);
+      }
+      reads(j % C::STAGES, t + 1, na, nb);
+      mfmas(ca, cb);
+      if (t == 0) step_hint<READS, MFMAS, ALL_DMA ? Part1::COUNT : 0>();
+      else if (t == 1) step_hint<READS, MFMAS, ALL_DMA ? Part2::COUNT : 0>();
+      else if (t == 2) step_hint<READS, MFMAS, ALL_DMA ? Part3::COUNT : 0>();
+      else step_hint<READS, MFMAS, 0>();
     }
   };
 
-  // ---- main loop over a ring of STAGES LDS buffers
   if (nk > 0) {
+    // Prologue: slices 0..STAGES-2 in flight, then "boundary -1" publishes
+    // slice 0 and the first k-step's fragments are read.
 #pragma unroll
     for (int s = 0; s < C::STAGES - 1; ++s) {
       fetch(s, k_begin + s * C::BKE);
       commit(s);
     }
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    // This wave's DMA loads of slice kt are complete once no more than the
-    // loads of the STAGES-2 later slices are outstanding; its LDS writes (the
-    // register loaders' commits) are complete at lgkmcnt(0). Then one barrier
-    // publishes slice kt to every wave. (A plain __syncthreads would also wait
-    // for the later slices' loads.)
-    if constexpr (DMA_BEHIND == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (DMA_BEHIND == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (DMA_BEHIND == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (DMA_BEHIND == 6) asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (DMA_BEHIND == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (DMA_BEHIND == 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if constexpr (DMA_BEHIND == 16) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // The buffer of slice kt+STAGES-1 held slice kt-1, which every wave has
-    // finished with (it passed the barrier above). Past the end of K the
-    // loads read zeros, which keeps the number of loads per slice constant.
-    const int nxt = kt + C::STAGES - 1;
-    const int st_next = nxt % C::STAGES;
-    fetch(st_next, k_begin + nxt * C::BKE);
-    compute(kt % C::STAGES);
-    commit(st_next);
+    wait_loads_and_barrier<DMA_BEHIND>();
+    fetch(C::STAGES - 1, k_begin + (C::STAGES - 1) * C::BKE);
+    reads(0, 0, fa0, fb0);
+    // Slices are taken U at a time so that each loop iteration holds an even
+    // number of k-steps and the two fragment sets alternate statically. With
+    // U = 2 and nk odd the last pass runs on slice nk, whose loads read zeros:
+    // it adds exact zeros.
+    constexpr int U = C::KSTEPS % 2 == 0 ? 1 : 2;
+    for (int j0 = 0; j0 < nk; j0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < C::KSTEPS; ++t) {
+          if (((u * C::KSTEPS + t) & 1) == 0) step(j0 + u, t, fa0, fb0, fa1, fb1);
+          else step(j0 + u, t, fa1, fb1, fa0, fb0);
+        }
+    }
   }
 
   // The LDS ring becomes the epilogue's staging area: wait until no load into
@@ -528,19 +688,7 @@ gemm_tile_kernel(GemmArgs p) {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   float* elds = reinterpret_cast<float*>(smem + wave * EpiLayout<C>::WAVE_BYTES);
   const int row0 = m0 + wm0, col0 = n0 + wn0;
-  if constexpr (SPLIT) {
-    epilogue<C, OUT_BF16, true, ACT_NONE>(p, acc, elds, row0, col0, lane, split);
-  } else {
-    const int act = p.act;
-    if (act == ACT_NONE)
-      epilogue<C, OUT_BF16, false, ACT_NONE>(p, acc, elds, row0, col0, lane, split);
-    else if (act == ACT_RELU)
-      epilogue<C, OUT_BF16, false, ACT_RELU>(p, acc, elds, row0, col0, lane, split);
-    else if (act == ACT_GELU_ERF)
-      epilogue<C, OUT_BF16, false, ACT_GELU_ERF>(p, acc, elds, row0, col0, lane, split);
-    else
-      epilogue<C, OUT_BF16, false, ACT_GELU_TANH>(p, acc, elds, row0, col0, lane, split);
-  }
+  run_epilogue<C, OUT_BF16, SPLIT>(p, acc, elds, row0, col0, lane, split);
 }
 
 // ----------------------------------------------------------- split-K reduction
@@ -585,12 +733,16 @@ static hipError_t launch_cfg(const Plan& plan, const LaunchSpec& spec, const Gem
   return hipGetLastError();
 }
 
-// Tile shapes in use: 128-byte K slices, two LDS stages. (Measured at
-// 4096^3: three or four stages of 64-byte slices were slower.)
-using Big16 = TileCfg<256, 256, 2, 4, false, 128, 2>;
-using Big8 = TileCfg<256, 256, 2, 4, true, 128, 2>;
-using Mid16 = TileCfg<256, 128, 4, 2, false, 128, 2>;
-using Mid8 = TileCfg<256, 128, 4, 2, true, 128, 2>;
+// Tile shapes in use. 256x256 (one workgroup per CU): 128-byte K slices
+// (64 BF16 / 128 FP8 elements) in two LDS stages; BF16 spreads each slice's
+// loads over three k-steps, FP8 issues them at once. Measured at 4096^3:
+// 128-byte slices beat 64-byte ones in a deeper ring (a 64-byte row is half
+// a cache line, so twice the L2 requests), and four waves of 128x128 lost to
+// eight waves of 128x64.
+using Big16 = TileCfg<256, 256, 2, 4, false, 128, 2, 3>;
+using Big8 = TileCfg<256, 256, 2, 4, true, 128, 2, 1>;
+using Mid16 = TileCfg<256, 128, 4, 2, false, 128, 2, 2>;
+using Mid8 = TileCfg<256, 128, 4, 2, true, 128, 2, 2>;
 using Small16 = TileCfg<128, 128, 2, 2, false, 128, 2>;
 using Small8 = TileCfg<128, 128, 2, 2, true, 128, 2>;
 

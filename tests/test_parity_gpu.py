@@ -42,6 +42,19 @@ def test_bf16_k_major_shapes(M, N, K):
     compare(p, run(p))
 
 
+# K a multiple of the 16-byte chunk but not of the K slice (64 BF16 / 128 FP8
+# elements): the copy path's last slice is partial and its tail reads zeros.
+# Padded leading dimensions put NaN codes right after K, so a tail that is not
+# zeroed shows up as NaN.
+@pytest.mark.parametrize("kind,M,N,K", [("bf16", 260, 300, 72), ("bf16", 512, 512, 4096 + 24),
+                                        ("fp8", 300, 260, 208), ("fp8", 257, 513, 336),
+                                        ("fp8", 512, 512, 2048 + 48)])
+def test_partial_last_k_slice(kind, M, N, K):
+    p = synth.make_problem(kind, M, N, K, seed_base=0x110000 + M + K, lda=K + 64, ldb=K + 32,
+                           c_dtype=OUT_F32, bias_std=0.1)
+    compare(p, run(p))
+
+
 @pytest.mark.parametrize("la,lb", [(ROW, ROW), (ROW, COL), (COL, ROW), (COL, COL)])
 @pytest.mark.parametrize("M,N,K", [(190, 250, 200), (130, 260, 333)])
 def test_bf16_all_layouts(la, lb, M, N, K):
