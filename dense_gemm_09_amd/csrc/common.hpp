@@ -44,12 +44,18 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// FP32 -> BF16 bits, round to nearest even; NaN stays a quiet NaN.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// FP32 -> BF16 bits, round to nearest even (gfx950's v_cvt_pk_bf16_f32; a
+// NaN stays a quiet NaN). Two values per instruction.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return static_cast<uint16_t>(f32x2_to_bf16x2_bits(f, 0.f));
 }
 
 // ---------------------------------------------------------------- epilogue math
@@ -79,7 +85,10 @@ __device__ __forceinline__ float erf_as7126(float x) {
 
 __device__ __forceinline__ float apply_act(float z, int act) {
   if (act == ACT_RELU) return z > 0.f ? z : 0.f;
-  if (act == ACT_GELU_ERF) return 0.5f * z * (1.f + erf_as7126(z * 0.70710678118654752f));
+  if (act == ACT_GELU_ERF) {
+    const float hz = 0.5f * z;
+    return fmaf(hz, erf_as7126(z * 0.70710678118654752f), hz);
+  }
   if (act == ACT_GELU_TANH) {
     // tanh(u) = 1 - 2 / (1 + e^(2u)); saturates correctly for large |u|.
     const float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);  // sqrt(2/pi) (...)

@@ -323,13 +323,16 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
   const int n = col0 + 4 * cq;
   const bool vec_ok = p.c_vec != 0 && n + 3 < N;
 
-  // Per-column factors, fixed for this lane.
-  float sb[4] = {1.f, 1.f, 1.f, 1.f}, bias_v[4] = {0.f, 0.f, 0.f, 0.f};
+  // Per-column factors, fixed for this lane: alpha * scale_b[n] and bias[n].
+  // An element is then fma(acc, scale_a[m] * cs[q], bias[q]) (+ beta * C_in).
+  float cs[4], bias_v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) cs[q] = p.alpha;
   if constexpr (!SPLIT) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (n + q < N) {
-        if constexpr (C::FP8) sb[q] = p.scale_b[n + q];
+        if constexpr (C::FP8) cs[q] = p.alpha * p.scale_b[n + q];
         if (p.bias) bias_v[q] = bf16_bits_to_f32(p.bias[n + q]);
       }
     }
@@ -395,25 +398,28 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
         }
         continue;
       } else {
-        const float sa = C::FP8 ? p.scale_a[m] : 1.f;
         const float4 cc = cin[i & 1][it];
         const float c4[4] = {cc.x, cc.y, cc.z, cc.w};
+        if constexpr (C::FP8) {
+          const float sa = p.scale_a[m];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = fmaf(v[q], sa * cs[q], bias_v[q]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = fmaf(v[q], cs[q], bias_v[q]);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float z = v[q];
-          if constexpr (C::FP8) z = z * (sa * sb[q]);
-          z = p.alpha * z;
-          if (p.beta != 0.f) z += p.beta * c4[q];
-          v[q] = apply_act(z + bias_v[q], ACT);
+          if (use_c) z = fmaf(p.beta, c4[q], z);
+          v[q] = apply_act(z, ACT);
         }
         const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
         if (vec_ok) {
           if constexpr (OUT_BF16) {
             uint2 h;
-            h.x = static_cast<uint32_t>(f32_to_bf16_bits(v[0])) |
-                  (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
-            h.y = static_cast<uint32_t>(f32_to_bf16_bits(v[2])) |
-                  (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+            h.x = f32x2_to_bf16x2_bits(v[0], v[1]);
+            h.y = f32x2_to_bf16x2_bits(v[2], v[3]);
             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.C) + off) = h;
           } else {
             *reinterpret_cast<float4*>(static_cast<float*>(p.C) + off) =
