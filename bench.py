@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB device copy (counter "
                          "calibration) then 3 launches of each headline GEMM")
-    ap.add_argument("--only", default="", help="comma list of extra groups: decode,ffn,ragged,proj")
+    ap.add_argument("--only", default="", help="comma list of extra groups: decode,ffn,ragged,proj,quant")
     return ap.parse_args()
 
 
@@ -247,7 +247,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extras:
-        only = set(args.only.split(",")) if args.only else {"decode", "ffn", "ragged", "proj"}
+        only = set(args.only.split(",")) if args.only else {"decode", "ffn", "ragged", "proj", "quant"}
         extra.update(run_extras(only))
 
     cpu = None
@@ -269,6 +269,7 @@ def main():
 
 
 def run_extras(only):
+    import numpy as np
     import torch
     from synth import workloads
     res = {}
@@ -301,6 +302,34 @@ def run_extras(only):
         for M in workloads.FFN_M:
             for N, K in workloads.FFN_SHAPES:
                 measure(f"ffn_bf16_{M}x{N}x{K}", workloads.ffn(M, N, K), steps=10, warmup=3)
+    if "quant" in only:
+        # Per-token FP8 quantisation of BF16 activations (the FP8 GEMM's A
+        # operand): the projection's 4096 x 2048 and an FFN's 8192 x 4096.
+        # HBM-bound: 2 bytes read + 1 byte written per element + 4 per row.
+        import dense_gemm_09_amd as g
+        import synth
+        for M, K in ((4096, 2048), (8192, 4096)):
+            x = synth.to_bf16_bits(synth.normal((M, K), 1.0, 0x5EED9000 + M))
+            base = torch.from_numpy(x.view(np.int16)).cuda()
+            n = 1 if NO_ROTATE else int(max(1, np.ceil(ROTATE_BYTES / (3 * M * K))))
+            xs = [base] + [base.clone() for _ in range(n - 1)]
+            qs = [torch.empty((M, K), dtype=torch.uint8, device="cuda") for _ in range(n)]
+            ss = [torch.empty(M, dtype=torch.float32, device="cuda") for _ in range(n)]
+            state = {"i": 0}
+
+            def call():
+                i = state["i"] % n
+                state["i"] += 1
+                g.quantize_fp8_rows(M, K, xs[i], K, qs[i], K, ss[i])
+
+            us = time_graph(call, calls=4 * n) * 1e3
+            by = 3 * M * K + 4 * M
+            r = {"us": round(us, 2), "gbps": round(by / (us * 1e-6) / 1e9, 0),
+                 "frac_hbm": round(by / (us * 1e-6) / 1e9 / HBM_GBPS, 4)}
+            res[f"quant_fp8_rows_{M}x{K}"] = r
+            log(f"[bench] quant_fp8_rows_{M}x{K}: {r}")
+            del xs, qs, ss
+            torch.cuda.empty_cache()
     if "ragged" in only:
         for kind in ("bf16", "fp8"):
             for padded in (False, True):

@@ -25,8 +25,8 @@ ACT_NONE, ACT_RELU, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2, 3
 STATUS = ["GEMM_OK", "GEMM_ERR_NULL_POINTER", "GEMM_ERR_BAD_DIM", "GEMM_ERR_BAD_LD",
           "GEMM_ERR_BAD_ENUM", "GEMM_ERR_UNSUPPORTED", "GEMM_ERR_WORKSPACE_TOO_SMALL",
           "GEMM_ERR_HIP"]
-EXPORTS = ["gemm_bf16", "gemm_fp8_scaled", "gemm_workspace_size", "gemm_plan",
-           "gemm_status_string"]
+EXPORTS = ["gemm_bf16", "gemm_fp8_scaled", "gemm_quantize_fp8_rows", "gemm_workspace_size",
+           "gemm_plan", "gemm_status_string"]
 
 
 class GemmError(RuntimeError):
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_fp8_scaled.restype = _I32
         L.gemm_fp8_scaled.argtypes = [_I64, _I64, _I64, _F32, _P, _I64, _I32, _P, _I64, _I32,
                                       _P, _P, _F32, _P, _I64, _I32, _P, _I32, _P, _SZ, _P]
+        L.gemm_quantize_fp8_rows.restype = _I32
+        L.gemm_quantize_fp8_rows.argtypes = [_I64, _I64, _P, _I64, _P, _I64, _P, _P]
         L.gemm_workspace_size.restype = _SZ
         L.gemm_workspace_size.argtypes = [_I64, _I64, _I64, _I32]
         L.gemm_plan.restype = _I32
@@ -165,6 +167,19 @@ def gemm_fp8_scaled(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, scale_a,
                            _ptr(bias), act, _ptr(workspace), workspace_bytes, _stream(stream))
     if st != 0:
         raise GemmError(st, "gemm_fp8_scaled")
+
+
+def quantize_fp8_rows(M, K, X, ldx, Q, ldq, scale, stream=None):
+    """Per-token E4M3 quantisation of BF16 rows: scale[m] = amax/448, Q = e4m3(x / scale)."""
+    L = lib()
+    if M > 0 and K > 0:
+        _need(X, 2 * _extent(M, K, ldx), "X")
+        _need(Q, _extent(M, K, ldq), "Q")
+    if M > 0:
+        _need(scale, 4 * M, "scale")
+    st = L.gemm_quantize_fp8_rows(M, K, _ptr(X), ldx, _ptr(Q), ldq, _ptr(scale), _stream(stream))
+    if st != 0:
+        raise GemmError(st, "gemm_quantize_fp8_rows")
 
 
 def _workspace(M, N, K, fp8, workspace, workspace_bytes, like):

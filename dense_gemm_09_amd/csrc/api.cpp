@@ -234,6 +234,22 @@ gemm_status gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, float alpha, const 
              C, ldc, c_dtype, bias, act, workspace, workspace_bytes, stream);
 }
 
+gemm_status gemm_quantize_fp8_rows(int64_t M, int64_t K, const void* X, int64_t ldx, void* Q,
+                                   int64_t ldq, float* scale, void* stream) {
+  if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim) return GEMM_ERR_BAD_DIM;
+  if (ldx < std::max<int64_t>(1, K) || ldq < std::max<int64_t>(1, K)) return GEMM_ERR_BAD_LD;
+  if (M == 0) return GEMM_OK;
+  if (scale == nullptr) return GEMM_ERR_NULL_POINTER;
+  if (K > 0 && (X == nullptr || Q == nullptr)) return GEMM_ERR_NULL_POINTER;
+  const auto aligned = [](const void* p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+  };
+  const bool vec = K % 8 == 0 && ldx % 8 == 0 && ldq % 8 == 0 && aligned(X, 16) && aligned(Q, 8);
+  return launch_quantize_rows(M, K, X, ldx, Q, ldq, scale, vec,
+                              static_cast<hipStream_t>(stream)) == hipSuccess
+             ? GEMM_OK : GEMM_ERR_HIP;
+}
+
 size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int is_fp8) {
   if (M <= 0 || N <= 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   return make_plan(M, N, K, is_fp8 != 0).workspace;

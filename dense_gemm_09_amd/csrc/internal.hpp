@@ -45,4 +45,9 @@ hipError_t launch_skinny(const Plan& plan, const LaunchSpec& spec, const GemmArg
 hipError_t launch_splitk_reduce(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
                                 hipStream_t stream);
 
+// Per-token FP8 quantisation of BF16 rows (quant.hip). vec: 16-byte aligned
+// rows with K and ldx multiples of 8 and Q rows 8-byte aligned.
+hipError_t launch_quantize_rows(int64_t M, int64_t K, const void* X, int64_t ldx, void* Q,
+                                int64_t ldq, float* scale, bool vec, hipStream_t stream);
+
 }  // namespace g355

@@ -1,0 +1,137 @@
+// Per-token FP8 quantisation of BF16 activations: the step that produces the
+// FP8 GEMM's A operand and its per-row scales.
+//
+// The FP8 DeepGEMM page (sec. 1.2) pairs E4M3 activations with one scale per
+// token and observes that scale handling done in separate kernels costs extra
+// launches and extra trips through memory. Here one workgroup owns one row and
+// produces its scale and its codes in a single launch, reading the row from
+// HBM once:
+//
+//   scale[m] = fp32(amax_k |x(m,k)| / 448)      (1 for an all-zero row)
+//   Q[m, k]  = E4M3 code of RNE(x(m,k) / scale[m]), saturating at +-448
+//
+// The division is IEEE float32 division (correctly rounded), so the quotient
+// that decides each code is the same float32 value any IEEE implementation
+// computes; the float32 -> E4M3 step is gfx950's v_cvt_pk_fp8_f32 (round to
+// nearest even) after clamping to +-448. |x| / scale exceeds 448 by at most a
+// rounding error, so the clamp only ever maps such values to 448.
+//
+// One wave owns one row. A row of up to 4096 elements is loaded once into
+// registers (all of a lane's loads issued before any is used), reduced to its
+// amax with cross-lane shuffles, and encoded from the registers; longer rows
+// re-read their tail from cache. HBM traffic is 2 bytes read + 1 byte written
+// per element.
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace g355 {
+
+constexpr int kQuantThreads = 256;   // four waves, one row each
+constexpr int kChunk = 512;          // elements of a row one wave covers per 16-byte load
+constexpr int kCached = 8;           // chunks kept in registers (rows up to 4096 elements)
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Four float32 quotients -> four E4M3 codes in one 32-bit word (byte q holds
+// element q).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const float lim = 448.f;
+  a = __builtin_amdgcn_fmed3f(a, -lim, lim);
+  b = __builtin_amdgcn_fmed3f(b, -lim, lim);
+  c = __builtin_amdgcn_fmed3f(c, -lim, lim);
+  d = __builtin_amdgcn_fmed3f(d, -lim, lim);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+__device__ __forceinline__ float amax8(float amax, const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    amax = fmaxf(amax, fabsf(__uint_as_float(w[j] << 16)));
+    amax = fmaxf(amax, fabsf(__uint_as_float(w[j] & 0xffff0000u)));
+  }
+  return amax;
+}
+
+__device__ __forceinline__ uint2 codes8(const uint4& v, float s) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[2 * j] = __uint_as_float(w[j] << 16) / s;
+    f[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u) / s;
+  }
+  return make_uint2(e4m3x4(f[0], f[1], f[2], f[3]), e4m3x4(f[4], f[5], f[6], f[7]));
+}
+
+// One wave per row. VEC: 16-byte loads of 8 BF16 and 8-byte stores of 8
+// codes; the first kCached chunks of the row are loaded up front and kept in
+// registers for the second pass (longer rows re-read the rest, from cache);
+// otherwise element by element.
+template <bool VEC>
+__global__ void __launch_bounds__(kQuantThreads)
+quantize_rows_kernel(const uint16_t* __restrict__ X, int64_t ldx, uint8_t* __restrict__ Q,
+                     int64_t ldq, float* __restrict__ scale, int M, int K) {
+  const int lane = threadIdx.x & 63;
+  const int m = blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6);
+  if (m >= M) return;  // no barrier below: a wave may leave early
+  const uint16_t* x = X + static_cast<int64_t>(m) * ldx;
+  uint8_t* q = Q + static_cast<int64_t>(m) * ldq;
+
+  float amax = 0.f;
+  if constexpr (VEC) {
+    uint4 c[kCached];
+#pragma unroll
+    for (int ch = 0; ch < kCached; ++ch) {
+      const int k = ch * kChunk + 8 * lane;
+      c[ch] = k < K ? *reinterpret_cast<const uint4*>(x + k) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int ch = 0; ch < kCached; ++ch) amax = amax8(amax, c[ch]);
+    for (int k = kCached * kChunk + 8 * lane; k < K; k += kChunk)
+      amax = amax8(amax, *reinterpret_cast<const uint4*>(x + k));
+    amax = wave_max(amax);
+    const float s = amax > 0.f ? amax / 448.f : 1.f;
+    if (lane == 0) scale[m] = s;
+#pragma unroll
+    for (int ch = 0; ch < kCached; ++ch) {
+      const int k = ch * kChunk + 8 * lane;
+      if (k < K) *reinterpret_cast<uint2*>(q + k) = codes8(c[ch], s);
+    }
+    for (int k = kCached * kChunk + 8 * lane; k < K; k += kChunk)
+      *reinterpret_cast<uint2*>(q + k) = codes8(*reinterpret_cast<const uint4*>(x + k), s);
+  } else {
+    for (int k = lane; k < K; k += 64) amax = fmaxf(amax, fabsf(bf16_bits_to_f32(x[k])));
+    amax = wave_max(amax);
+    const float s = amax > 0.f ? amax / 448.f : 1.f;
+    if (lane == 0) scale[m] = s;
+    for (int k = lane; k < K; k += 64) {
+      const float y = bf16_bits_to_f32(x[k]) / s;
+      q[k] = static_cast<uint8_t>(e4m3x4(y, 0.f, 0.f, 0.f) & 0xffu);
+    }
+  }
+}
+
+hipError_t launch_quantize_rows(int64_t M, int64_t K, const void* X, int64_t ldx, void* Q,
+                                int64_t ldq, float* scale, bool vec, hipStream_t stream) {
+  const int rows_per_wg = kQuantThreads / 64;
+  const dim3 grid(static_cast<unsigned>((M + rows_per_wg - 1) / rows_per_wg)), block(kQuantThreads);
+  if (vec)
+    hipLaunchKernelGGL((quantize_rows_kernel<true>), grid, block, 0, stream,
+                       static_cast<const uint16_t*>(X), ldx, static_cast<uint8_t*>(Q), ldq, scale,
+                       static_cast<int>(M), static_cast<int>(K));
+  else
+    hipLaunchKernelGGL((quantize_rows_kernel<false>), grid, block, 0, stream,
+                       static_cast<const uint16_t*>(X), ldx, static_cast<uint8_t*>(Q), ldq, scale,
+                       static_cast<int>(M), static_cast<int>(K));
+  return hipGetLastError();
+}
+
+}  // namespace g355

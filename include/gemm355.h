@@ -106,6 +106,24 @@ gemm_status gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, float alpha,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Per-token FP8 quantisation of BF16 activations, producing the A operand and
+ * scale_a of gemm_fp8_scaled (the per-token scaling of DeepGEMM: FP8 precision
+ * Tensor Core GEMM optimisation, sec. 1.2, done in one pass per row instead of
+ * separate scale and cast kernels). For each row m of X:
+ *   scale[m]   = fp32(max_k |x(m,k)| / 448), or 1 if the row is all zero
+ *   Q[m*ldq+k] = OCP E4M3FN code of x(m,k) / scale[m] (IEEE float32 division,
+ *                round to nearest even, saturating at +-448)
+ * X: BF16, M x K row-major, ldx >= K (device). Q: uint8, M x K row-major,
+ * ldq >= K (device). scale: FP32[M] (device). Columns K..ld-1 are neither read
+ * nor written. K == 0 writes scale = 1 for every row. NaN or infinite inputs
+ * give undefined codes and scales. Errors: GEMM_ERR_BAD_DIM (M or K negative
+ * or above 2^30), GEMM_ERR_BAD_LD, GEMM_ERR_NULL_POINTER (scale, or X / Q when
+ * K > 0), GEMM_ERR_HIP; all checks run before anything is enqueued.
+ */
+gemm_status gemm_quantize_fp8_rows(int64_t M, int64_t K, const void* X, int64_t ldx,
+                                   void* Q, int64_t ldq, float* scale, void* stream);
+
+/*
  * Bytes of device workspace a call with these sizes needs (0 when the chosen
  * kernel needs none). Pure host arithmetic; callable without a GPU. Query
  * once and allocate up front (the FP8 page's interface, sec. 5.1, separates

@@ -160,3 +160,22 @@ def test_binding_rejects_short_tensors_before_calling():
     A = torch.zeros(10, dtype=torch.int16)
     with pytest.raises(ValueError):
         g._need(A, 1000, "A")  # CPU tensor is rejected as well
+
+
+def quant(M=64, K=64, X=FAKE, ldx=None, Q=FAKE, ldq=None, scale=FAKE):
+    ldx = K if ldx is None else ldx
+    ldq = K if ldq is None else ldq
+    return g.lib().gemm_quantize_fp8_rows(M, K, X, ldx, Q, ldq, scale, None)
+
+
+def test_quantizer_validation_before_launch():
+    assert quant(M=-1) == BAD_DIM
+    assert quant(K=-1) == BAD_DIM
+    assert quant(M=1 << 31) == BAD_DIM
+    assert quant(ldx=63) == BAD_LD
+    assert quant(ldq=63) == BAD_LD
+    assert quant(scale=None) == NULLP
+    assert quant(X=None) == NULLP
+    assert quant(Q=None) == NULLP
+    # M == 0: nothing to do, no pointer is touched
+    assert quant(M=0, X=None, Q=None, scale=None) == OK
