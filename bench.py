@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB device copy (counter "
                          "calibration) then 3 launches of each headline GEMM")
-    ap.add_argument("--only", default="", help="comma list of extra groups: decode,ffn,ragged,proj,quant")
+    ap.add_argument("--only", default="", help="comma list of extra groups: decode,ffn,ragged,proj,quant,qout")
     return ap.parse_args()
 
 
@@ -247,7 +247,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extras:
-        only = set(args.only.split(",")) if args.only else {"decode", "ffn", "ragged", "proj", "quant"}
+        only = set(args.only.split(",")) if args.only else {"decode", "ffn", "ragged", "proj", "quant", "qout"}
         extra.update(run_extras(only))
 
     cpu = None
@@ -330,6 +330,35 @@ def run_extras(only):
             log(f"[bench] quant_fp8_rows_{M}x{K}: {r}")
             del xs, qs, ss
             torch.cuda.empty_cache()
+    if "qout" in only:
+        # The FP8 projection (4096 x 7168 x 2048, bias, GELU) with the
+        # quantising epilogue: one byte per output element instead of BF16's
+        # two, no separate quantisation pass.
+        import dense_gemm_09_amd as g
+        p = workloads.fp8_projection()
+        w = Workload(p, copies_for(p))
+        qs = [torch.empty((p.M, p.N), dtype=torch.uint8, device="cuda") for _ in w.sets]
+        osc = torch.full((p.M,), 24.0, dtype=torch.float32, device="cuda")
+        ozp = torch.zeros(p.M, dtype=torch.int32, device="cuda")
+        for q_dtype, tag in ((g.QOUT_INT8, "int8"), (g.QOUT_E4M3, "e4m3")):
+            state = {"i": 0}
+
+            def call():
+                i = state["i"] % len(w.sets)
+                state["i"] += 1
+                d = w.sets[i]
+                g.gemm_fp8_scaled_quant(p.M, p.N, p.K, 1.0, d["A"], p.lda, p.layout_a, d["B"],
+                                        p.ldb, p.layout_b, d["scale_a"], d["scale_b"], d["bias"],
+                                        p.act, osc, ozp if q_dtype == g.QOUT_INT8 else None,
+                                        qs[i], p.N, q_dtype, workspace=w.ws)
+
+            per, _, _ = time_calls([call], 30, 5)
+            us = per[0] * 1e3
+            r = {"us": round(us, 2), "tflops": round(p.flops / (us * 1e-6) / 1e12, 1)}
+            res[f"fp8_4096x7168x2048_q{tag}"] = r
+            log(f"[bench] fp8_4096x7168x2048_q{tag}: {r}")
+        del w, qs
+        torch.cuda.empty_cache()
     if "ragged" in only:
         for kind in ("bf16", "fp8"):
             for padded in (False, True):

@@ -20,13 +20,14 @@ LIB_PATH = os.path.join(PKG, "libgemm355.so")
 
 ROW, COL = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
+QOUT_INT8, QOUT_E4M3 = 0, 1
 ACT_NONE, ACT_RELU, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2, 3
 
 STATUS = ["GEMM_OK", "GEMM_ERR_NULL_POINTER", "GEMM_ERR_BAD_DIM", "GEMM_ERR_BAD_LD",
           "GEMM_ERR_BAD_ENUM", "GEMM_ERR_UNSUPPORTED", "GEMM_ERR_WORKSPACE_TOO_SMALL",
           "GEMM_ERR_HIP"]
-EXPORTS = ["gemm_bf16", "gemm_fp8_scaled", "gemm_quantize_fp8_rows", "gemm_workspace_size",
-           "gemm_plan", "gemm_status_string"]
+EXPORTS = ["gemm_bf16", "gemm_fp8_scaled", "gemm_bf16_quant", "gemm_fp8_scaled_quant",
+           "gemm_quantize_fp8_rows", "gemm_workspace_size", "gemm_plan", "gemm_status_string"]
 
 
 class GemmError(RuntimeError):
@@ -61,6 +62,13 @@ def lib() -> ctypes.CDLL:
         L.gemm_fp8_scaled.restype = _I32
         L.gemm_fp8_scaled.argtypes = [_I64, _I64, _I64, _F32, _P, _I64, _I32, _P, _I64, _I32,
                                       _P, _P, _F32, _P, _I64, _I32, _P, _I32, _P, _SZ, _P]
+        L.gemm_bf16_quant.restype = _I32
+        L.gemm_bf16_quant.argtypes = [_I64, _I64, _I64, _F32, _P, _I64, _I32, _P, _I64, _I32,
+                                      _P, _I32, _P, _P, _P, _I64, _I32, _P, _SZ, _P]
+        L.gemm_fp8_scaled_quant.restype = _I32
+        L.gemm_fp8_scaled_quant.argtypes = [_I64, _I64, _I64, _F32, _P, _I64, _I32, _P, _I64,
+                                            _I32, _P, _P, _P, _I32, _P, _P, _P, _I64, _I32, _P,
+                                            _SZ, _P]
         L.gemm_quantize_fp8_rows.restype = _I32
         L.gemm_quantize_fp8_rows.argtypes = [_I64, _I64, _P, _I64, _P, _I64, _P, _P]
         L.gemm_workspace_size.restype = _SZ
@@ -167,6 +175,47 @@ def gemm_fp8_scaled(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, scale_a,
                            _ptr(bias), act, _ptr(workspace), workspace_bytes, _stream(stream))
     if st != 0:
         raise GemmError(st, "gemm_fp8_scaled")
+
+
+def _check_quant_out(M, N, Q, ldq, out_scale, out_zero):
+    if M > 0 and N > 0:
+        _need(Q, _extent(M, N, ldq), "Q")
+        _need(out_scale, 4 * M, "out_scale")
+        _need(out_zero, 4 * M, "out_zero")
+
+
+def gemm_bf16_quant(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, bias, act, out_scale,
+                    out_zero, Q, ldq, q_dtype, workspace=None, workspace_bytes=None,
+                    stream=None):
+    """Q = quant(act(alpha * A B + bias)) per row: INT8 (scale, zero point) or E4M3 (scale)."""
+    L = lib()
+    _check_operands(M, N, K, A, lda, layout_a, B, ldb, layout_b, None, ldq, OUT_BF16, 2, bias)
+    _check_quant_out(M, N, Q, ldq, out_scale, out_zero)
+    workspace, workspace_bytes = _workspace(M, N, K, False, workspace, workspace_bytes, Q)
+    st = L.gemm_bf16_quant(M, N, K, alpha, _ptr(A), lda, layout_a, _ptr(B), ldb, layout_b,
+                           _ptr(bias), act, _ptr(out_scale), _ptr(out_zero), _ptr(Q), ldq,
+                           q_dtype, _ptr(workspace), workspace_bytes, _stream(stream))
+    if st != 0:
+        raise GemmError(st, "gemm_bf16_quant")
+
+
+def gemm_fp8_scaled_quant(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, scale_a, scale_b,
+                          bias, act, out_scale, out_zero, Q, ldq, q_dtype, workspace=None,
+                          workspace_bytes=None, stream=None):
+    """Q = quant(act(alpha * scale_a[m] scale_b[n] * A B + bias)) per row, E4M3 inputs."""
+    L = lib()
+    _check_operands(M, N, K, A, lda, layout_a, B, ldb, layout_b, None, ldq, OUT_BF16, 1, bias)
+    _check_quant_out(M, N, Q, ldq, out_scale, out_zero)
+    if M > 0 and N > 0:
+        _need(scale_a, 4 * M, "scale_a")
+        _need(scale_b, 4 * N, "scale_b")
+    workspace, workspace_bytes = _workspace(M, N, K, True, workspace, workspace_bytes, Q)
+    st = L.gemm_fp8_scaled_quant(M, N, K, alpha, _ptr(A), lda, layout_a, _ptr(B), ldb, layout_b,
+                                 _ptr(scale_a), _ptr(scale_b), _ptr(bias), act, _ptr(out_scale),
+                                 _ptr(out_zero), _ptr(Q), ldq, q_dtype, _ptr(workspace),
+                                 workspace_bytes, _stream(stream))
+    if st != 0:
+        raise GemmError(st, "gemm_fp8_scaled_quant")
 
 
 def quantize_fp8_rows(M, K, X, ldx, Q, ldq, scale, stream=None):

@@ -112,16 +112,21 @@ namespace {
 bool valid_layout(int l) { return l == GEMM_ROW_MAJOR || l == GEMM_COL_MAJOR; }
 bool valid_out(int d) { return d == GEMM_OUT_F32 || d == GEMM_OUT_BF16; }
 bool valid_act(int a) { return a >= GEMM_ACT_NONE && a <= GEMM_ACT_GELU_TANH; }
+bool valid_qout(int q) { return q == GEMM_QOUT_INT8 || q == GEMM_QOUT_E4M3; }
+int qout_kind(int q) { return q == GEMM_QOUT_INT8 ? OUT_I8 : OUT_E4M3; }
 
+// out_kind: OutKind. The quantised kinds (INT8, E4M3) come with beta == 0,
+// the per-row output scale qscale and, for INT8 only, an optional zero point.
 gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
                 int64_t lda, int layout_a, const void* B, int64_t ldb, int layout_b,
                 const float* scale_a, const float* scale_b, float beta, void* C, int64_t ldc,
-                int c_dtype, const void* bias, int act, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                int out_kind, const float* qscale, const int32_t* qzero, const void* bias,
+                int act, void* workspace, size_t workspace_bytes, void* stream) {
   // ---- enums and sizes
-  if (!valid_layout(layout_a) || !valid_layout(layout_b) || !valid_out(c_dtype) ||
-      !valid_act(act))
+  if (!valid_layout(layout_a) || !valid_layout(layout_b) || !valid_act(act))
     return GEMM_ERR_BAD_ENUM;
+  const bool quant_out = out_kind == OUT_I8 || out_kind == OUT_E4M3;
+  if (out_kind == OUT_E4M3 && qzero != nullptr) return GEMM_ERR_UNSUPPORTED;
   if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
     return GEMM_ERR_BAD_DIM;
   if (fp8 && (layout_a != GEMM_ROW_MAJOR || layout_b != GEMM_COL_MAJOR))
@@ -137,6 +142,7 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   if (C == nullptr) return GEMM_ERR_NULL_POINTER;
   if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL_POINTER;
   if (fp8 && (scale_a == nullptr || scale_b == nullptr)) return GEMM_ERR_NULL_POINTER;
+  if (quant_out && qscale == nullptr) return GEMM_ERR_NULL_POINTER;
 
   const Plan plan = make_plan(M, N, K, fp8);
   // Every tile size in use is >= 128, so this bounds the grid of any variant.
@@ -153,7 +159,7 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   spec.fp8 = fp8;
   spec.a_kmajor = layout_a == GEMM_ROW_MAJOR;
   spec.b_kmajor = layout_b == GEMM_COL_MAJOR;
-  spec.out_bf16 = c_dtype == GEMM_OUT_BF16;
+  spec.out = out_kind;
   const bool k_ok = K % ce == 0;
   // The DMA loader addresses an operand with 32-bit byte offsets from its base
   // and marks chunks past K with an offset just beyond the operand's extent:
@@ -183,6 +189,8 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   a.scale_a = scale_a;
   a.scale_b = scale_b;
   a.workspace = static_cast<float*>(workspace);
+  a.qscale = quant_out ? qscale : nullptr;
+  a.qzero = out_kind == OUT_I8 ? qzero : nullptr;
   a.lda = lda;
   a.ldb = ldb;
   a.ldc = ldc;
@@ -190,11 +198,12 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   a.N = static_cast<int>(N);
   a.K = static_cast<int>(K);
   a.alpha = alpha;
-  a.beta = beta;
+  a.beta = quant_out ? 0.f : beta;
   a.act = act;
   {
     const uintptr_t cbase = reinterpret_cast<uintptr_t>(C);
-    const uintptr_t need = c_dtype == GEMM_OUT_F32 ? 16u : 8u;
+    // Bytes of one 4-element store: FP32 16, BF16 8, quantised 4.
+    const uintptr_t need = out_kind == OUT_F32 ? 16u : out_kind == OUT_BF16 ? 8u : 4u;
     a.c_vec = (cbase % need == 0 && ldc % 4 == 0) ? 1 : 0;
   }
   a.split_k = p.split;
@@ -220,8 +229,9 @@ gemm_status gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const void* 
                       gemm_layout layout_a, const void* B, int64_t ldb, gemm_layout layout_b,
                       float beta, void* C, int64_t ldc, gemm_out_dtype c_dtype, const void* bias,
                       gemm_act act, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_out(c_dtype)) return GEMM_ERR_BAD_ENUM;
   return run(false, M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, nullptr, nullptr, beta,
-             C, ldc, c_dtype, bias, act, workspace, workspace_bytes, stream);
+             C, ldc, c_dtype, nullptr, nullptr, bias, act, workspace, workspace_bytes, stream);
 }
 
 gemm_status gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, float alpha, const void* A,
@@ -230,8 +240,34 @@ gemm_status gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, float alpha, const 
                             float beta, void* C, int64_t ldc, gemm_out_dtype c_dtype,
                             const void* bias, gemm_act act, void* workspace,
                             size_t workspace_bytes, void* stream) {
+  if (!valid_out(c_dtype)) return GEMM_ERR_BAD_ENUM;
   return run(true, M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, scale_a, scale_b, beta,
-             C, ldc, c_dtype, bias, act, workspace, workspace_bytes, stream);
+             C, ldc, c_dtype, nullptr, nullptr, bias, act, workspace, workspace_bytes, stream);
+}
+
+gemm_status gemm_bf16_quant(int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                            int64_t lda, gemm_layout layout_a, const void* B, int64_t ldb,
+                            gemm_layout layout_b, const void* bias, gemm_act act,
+                            const float* out_scale, const int32_t* out_zero, void* Q,
+                            int64_t ldq, gemm_qout_dtype q_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!valid_qout(q_dtype)) return GEMM_ERR_BAD_ENUM;
+  return run(false, M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, nullptr, nullptr, 0.f,
+             Q, ldq, qout_kind(q_dtype), out_scale, out_zero, bias, act, workspace,
+             workspace_bytes, stream);
+}
+
+gemm_status gemm_fp8_scaled_quant(int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                                  int64_t lda, gemm_layout layout_a, const void* B, int64_t ldb,
+                                  gemm_layout layout_b, const float* scale_a,
+                                  const float* scale_b, const void* bias, gemm_act act,
+                                  const float* out_scale, const int32_t* out_zero, void* Q,
+                                  int64_t ldq, gemm_qout_dtype q_dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!valid_qout(q_dtype)) return GEMM_ERR_BAD_ENUM;
+  return run(true, M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, scale_a, scale_b, 0.f,
+             Q, ldq, qout_kind(q_dtype), out_scale, out_zero, bias, act, workspace,
+             workspace_bytes, stream);
 }
 
 gemm_status gemm_quantize_fp8_rows(int64_t M, int64_t K, const void* X, int64_t ldx, void* Q,

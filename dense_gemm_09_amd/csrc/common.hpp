@@ -17,6 +17,11 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 enum Act : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_ERF = 2, ACT_GELU_TANH = 3 };
 
+// What the epilogue writes: FP32 or BF16 C (read back when beta != 0), or a
+// quantised tensor of one byte per element with a per-row output scale
+// (INT8 with a per-row zero point, or OCP E4M3FN), never read.
+enum OutKind : int { OUT_F32 = 0, OUT_BF16 = 1, OUT_I8 = 2, OUT_E4M3 = 3 };
+
 // Everything a GEMM launch needs; passed by value as the kernel argument.
 struct GemmArgs {
   const void* A;
@@ -26,6 +31,8 @@ struct GemmArgs {
   const float* scale_a;   // FP32[M] (FP8 only)
   const float* scale_b;   // FP32[N] (FP8 only)
   float* workspace;       // split-K partials
+  const float* qscale;    // FP32[M] output scale (quantised outputs)
+  const int32_t* qzero;   // INT32[M] output zero point (INT8 output) or nullptr
   int64_t lda, ldb, ldc;
   int M, N, K;
   float alpha, beta;
@@ -56,6 +63,81 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>(f32x2_to_bf16x2_bits(f, 0.f));
+}
+
+// Four FP32 values -> four OCP E4M3FN codes in one word (byte q holds value q):
+// clamped to +-448, then gfx950's v_cvt_pk_fp8_f32 (round to nearest even).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const float lim = 448.f;
+  a = __builtin_amdgcn_fmed3f(a, -lim, lim);
+  b = __builtin_amdgcn_fmed3f(b, -lim, lim);
+  c = __builtin_amdgcn_fmed3f(c, -lim, lim);
+  d = __builtin_amdgcn_fmed3f(d, -lim, lim);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// INT8 output code of y: round to nearest even of fp32(y * s + zp) (one
+// rounding, fused multiply-add), saturated to [-128, 127]; low byte of the
+// result. Clamping before rounding gives the same code: the bounds are integers.
+__device__ __forceinline__ uint32_t quant_i8(float y, float s, float zp) {
+  const float v = __builtin_amdgcn_fmed3f(fmaf(y, s, zp), -128.f, 127.f);
+  return static_cast<uint32_t>(static_cast<int>(__builtin_rintf(v))) & 0xffu;
+}
+
+// Element `off` of an output of kind OUT. s and zp: the row's output scale and
+// zero point (quantised kinds only).
+template <int OUT>
+__device__ __forceinline__ void store_out1(void* C, int64_t off, float v, float s, float zp) {
+  if constexpr (OUT == OUT_F32) {
+    static_cast<float*>(C)[off] = v;
+  } else if constexpr (OUT == OUT_BF16) {
+    static_cast<uint16_t*>(C)[off] = f32_to_bf16_bits(v);
+  } else if constexpr (OUT == OUT_I8) {
+    static_cast<uint8_t*>(C)[off] = static_cast<uint8_t>(quant_i8(v, s, zp));
+  } else {
+    static_cast<uint8_t*>(C)[off] = static_cast<uint8_t>(e4m3x4(v * s, 0.f, 0.f, 0.f) & 0xffu);
+  }
+}
+
+// Elements off..off+3 in one store (16, 8 or 4 bytes, aligned by the caller).
+template <int OUT>
+__device__ __forceinline__ void store_out4(void* C, int64_t off, const float (&v)[4], float s,
+                                           float zp) {
+  if constexpr (OUT == OUT_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(C) + off) = make_float4(v[0], v[1], v[2], v[3]);
+  } else if constexpr (OUT == OUT_BF16) {
+    uint2 h;
+    h.x = f32x2_to_bf16x2_bits(v[0], v[1]);
+    h.y = f32x2_to_bf16x2_bits(v[2], v[3]);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(C) + off) = h;
+  } else if constexpr (OUT == OUT_I8) {
+    const uint32_t w = quant_i8(v[0], s, zp) | (quant_i8(v[1], s, zp) << 8) |
+                       (quant_i8(v[2], s, zp) << 16) | (quant_i8(v[3], s, zp) << 24);
+    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(C) + off) = w;
+  } else {
+    *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(C) + off) =
+        e4m3x4(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+  }
+}
+
+// The row's output scale and zero point (1 and 0 for unquantised kinds).
+template <int OUT>
+__device__ __forceinline__ void out_row_params(const GemmArgs& p, int m, float& s, float& zp) {
+  s = 1.f;
+  zp = 0.f;
+  if constexpr (OUT >= OUT_I8) s = p.qscale[m];
+  if constexpr (OUT == OUT_I8) {
+    if (p.qzero) zp = static_cast<float>(p.qzero[m]);
+  }
+}
+
+// C_in element as FP32 (only the FP32 and BF16 kinds are ever read).
+template <int OUT>
+__device__ __forceinline__ float load_cin1(const void* C, int64_t off) {
+  if constexpr (OUT == OUT_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(C)[off]);
+  else return static_cast<const float*>(C)[off];
 }
 
 // ---------------------------------------------------------------- epilogue math

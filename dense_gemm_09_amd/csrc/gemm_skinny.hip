@@ -39,7 +39,7 @@ struct SkinnyCfg {
   static constexpr int NT = KW * 64;
 };
 
-template <class S, bool OUT_BF16, int MB, int ACT>
+template <class S, int OUT, int MB, int ACT>
 __device__ __forceinline__ void skinny_epilogue(const GemmArgs& p, const f32x4 (&acc)[MB], int n0,
                                                 int lane) {
   const int n = n0 + (lane & 15);
@@ -57,19 +57,18 @@ __device__ __forceinline__ void skinny_epilogue(const GemmArgs& p, const f32x4 (
       if constexpr (S::ES == 1) z = z * (p.scale_a[m] * sb);
       z = p.alpha * z;
       const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
-      if (p.beta != 0.f) {
-        const float cin = OUT_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.C)[off])
-                                   : static_cast<const float*>(p.C)[off];
-        z += p.beta * cin;
+      if constexpr (OUT == OUT_F32 || OUT == OUT_BF16) {
+        if (p.beta != 0.f) z += p.beta * load_cin1<OUT>(p.C, off);
       }
       z = apply_act(z + bias_v, ACT);
-      if constexpr (OUT_BF16) static_cast<uint16_t*>(p.C)[off] = f32_to_bf16_bits(z);
-      else static_cast<float*>(p.C)[off] = z;
+      float qs, qz;
+      out_row_params<OUT>(p, m, qs, qz);
+      store_out1<OUT>(p.C, off, z, qs, qz);
     }
   }
 }
 
-template <bool FP8, int MB, int KW, int U, bool OUT_BF16>
+template <bool FP8, int MB, int KW, int U, int OUT>
 __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(GemmArgs p) {
   using S = SkinnyCfg<FP8, MB, KW, U>;
   __shared__ __attribute__((aligned(16))) f32x4 red[KW][MB][64];
@@ -161,24 +160,28 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(GemmArgs p) {
     acc[mb] = s;
   }
   const int act = p.act;
-  if (act == ACT_NONE) skinny_epilogue<S, OUT_BF16, MB, ACT_NONE>(p, acc, n0, lane);
-  else if (act == ACT_RELU) skinny_epilogue<S, OUT_BF16, MB, ACT_RELU>(p, acc, n0, lane);
-  else if (act == ACT_GELU_ERF) skinny_epilogue<S, OUT_BF16, MB, ACT_GELU_ERF>(p, acc, n0, lane);
-  else skinny_epilogue<S, OUT_BF16, MB, ACT_GELU_TANH>(p, acc, n0, lane);
+  if (act == ACT_NONE) skinny_epilogue<S, OUT, MB, ACT_NONE>(p, acc, n0, lane);
+  else if (act == ACT_RELU) skinny_epilogue<S, OUT, MB, ACT_RELU>(p, acc, n0, lane);
+  else if (act == ACT_GELU_ERF) skinny_epilogue<S, OUT, MB, ACT_GELU_ERF>(p, acc, n0, lane);
+  else skinny_epilogue<S, OUT, MB, ACT_GELU_TANH>(p, acc, n0, lane);
 }
 
 #ifndef G355_KERNELS_ONLY
 // KW = 16 K-split waves per workgroup; U k-steps of loads in flight per wave
 // (BF16 4 x 1 KB, FP8 2 x 2 KB). Chosen by a sweep at K = 4096, N = 4096..18432.
 template <bool FP8, int MB>
-static hipError_t launch_mb(const GemmArgs& a, bool out_bf16, hipStream_t stream) {
+static hipError_t launch_mb(const GemmArgs& a, int out, hipStream_t stream) {
   constexpr int KW = 16;
   constexpr int U = FP8 ? 2 : 4;
   const dim3 grid(static_cast<unsigned>((a.N + 15) / 16)), block(KW * 64);
-  if (out_bf16)
-    hipLaunchKernelGGL((gemm_skinny_kernel<FP8, MB, KW, U, true>), grid, block, 0, stream, a);
+  if (out == OUT_BF16)
+    hipLaunchKernelGGL((gemm_skinny_kernel<FP8, MB, KW, U, OUT_BF16>), grid, block, 0, stream, a);
+  else if (out == OUT_I8)
+    hipLaunchKernelGGL((gemm_skinny_kernel<FP8, MB, KW, U, OUT_I8>), grid, block, 0, stream, a);
+  else if (out == OUT_E4M3)
+    hipLaunchKernelGGL((gemm_skinny_kernel<FP8, MB, KW, U, OUT_E4M3>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((gemm_skinny_kernel<FP8, MB, KW, U, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_skinny_kernel<FP8, MB, KW, U, OUT_F32>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -186,8 +189,8 @@ hipError_t launch_skinny(const Plan& plan, const LaunchSpec& spec, const GemmArg
                          hipStream_t stream) {
   (void)plan;
   if (a.M > 16) return hipErrorInvalidValue;  // the plan only selects M <= 16
-  return spec.fp8 ? launch_mb<true, 1>(a, spec.out_bf16, stream)
-                  : launch_mb<false, 1>(a, spec.out_bf16, stream);
+  return spec.fp8 ? launch_mb<true, 1>(a, spec.out, stream)
+                  : launch_mb<false, 1>(a, spec.out, stream);
 }
 #endif  // G355_KERNELS_ONLY
 

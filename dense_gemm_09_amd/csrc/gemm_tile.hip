@@ -312,7 +312,7 @@ struct EpiLayout {
   static_assert(64 % CG == 0, "lanes per row");
 };
 
-template <class C, bool OUT_BF16, bool SPLIT, int ACT>
+template <class C, int OUT, bool SPLIT, int ACT>
 __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[C::FM][C::FN],
                                          float* lds, int row0, int col0, int lane, int split) {
   using E = EpiLayout<C>;
@@ -339,7 +339,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
   }
 
   // C_in of strip i+1 is requested before strip i is processed, so its HBM
-  // latency overlaps the epilogue math and stores of strip i.
+  // latency overlaps the epilogue math and stores of strip i. Quantised
+  // outputs have no C_in.
+  constexpr bool HAS_CIN = !SPLIT && (OUT == OUT_F32 || OUT == OUT_BF16);
   float4 cin[2][E::ITERS];
   auto load_cin = [&](int i, float4 (&dst)[E::ITERS]) {
 #pragma unroll
@@ -349,7 +351,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
       if (m >= M) continue;
       const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
       if (vec_ok) {
-        if constexpr (OUT_BF16) {
+        if constexpr (OUT == OUT_BF16) {
           const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.C) + off);
           dst[it] = make_float4(__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xffff0000u),
                                 __uint_as_float(h.y << 16), __uint_as_float(h.y & 0xffff0000u));
@@ -360,19 +362,21 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
         float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (n + q < N)
-            t[q] = OUT_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.C)[off + q])
-                            : static_cast<const float*>(p.C)[off + q];
+          if (n + q < N) t[q] = load_cin1<OUT>(p.C, off + q);
         dst[it] = make_float4(t[0], t[1], t[2], t[3]);
       }
     }
   };
-  const bool use_c = !SPLIT && p.beta != 0.f;
-  if (use_c) load_cin(0, cin[0]);
+  const bool use_c = HAS_CIN && p.beta != 0.f;
+  if constexpr (HAS_CIN) {
+    if (use_c) load_cin(0, cin[0]);
+  }
 
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
-    if (use_c && i + 1 < C::FM) load_cin(i + 1, cin[(i + 1) & 1]);
+    if constexpr (HAS_CIN) {
+      if (use_c && i + 1 < C::FM) load_cin(i + 1, cin[(i + 1) & 1]);
+    }
     // accumulators of rows 32i..32i+31 -> LDS strip
 #pragma unroll
     for (int j = 0; j < C::FN; ++j)
@@ -398,8 +402,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
         }
         continue;
       } else {
-        const float4 cc = cin[i & 1][it];
-        const float c4[4] = {cc.x, cc.y, cc.z, cc.w};
         if constexpr (C::FP8) {
           const float sa = p.scale_a[m];
 #pragma unroll
@@ -408,30 +410,24 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = fmaf(v[q], cs[q], bias_v[q]);
         }
+        if constexpr (HAS_CIN) {
+          const float4 cc = cin[i & 1][it];
+          const float c4[4] = {cc.x, cc.y, cc.z, cc.w};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float z = v[q];
-          if (use_c) z = fmaf(p.beta, c4[q], z);
-          v[q] = apply_act(z, ACT);
+          for (int q = 0; q < 4; ++q)
+            if (use_c) v[q] = fmaf(p.beta, c4[q], v[q]);
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = apply_act(v[q], ACT);
+        float qs, qz;
+        out_row_params<OUT>(p, m, qs, qz);
         const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
         if (vec_ok) {
-          if constexpr (OUT_BF16) {
-            uint2 h;
-            h.x = f32x2_to_bf16x2_bits(v[0], v[1]);
-            h.y = f32x2_to_bf16x2_bits(v[2], v[3]);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.C) + off) = h;
-          } else {
-            *reinterpret_cast<float4*>(static_cast<float*>(p.C) + off) =
-                make_float4(v[0], v[1], v[2], v[3]);
-          }
+          store_out4<OUT>(p.C, off, v, qs, qz);
         } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (n + q >= N) continue;
-            if constexpr (OUT_BF16) static_cast<uint16_t*>(p.C)[off + q] = f32_to_bf16_bits(v[q]);
-            else static_cast<float*>(p.C)[off + q] = v[q];
-          }
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) store_out1<OUT>(p.C, off + q, v[q], qs, qz);
         }
       }
     }
@@ -439,27 +435,27 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
 }
 
 // Runs the epilogue with the activation as a compile-time parameter.
-template <class C, bool OUT_BF16, bool SPLIT>
+template <class C, int OUT, bool SPLIT>
 __device__ __forceinline__ void run_epilogue(const GemmArgs& p, const f32x16 (&acc)[C::FM][C::FN],
                                              float* lds, int row0, int col0, int lane, int split) {
   if constexpr (SPLIT) {
-    epilogue<C, OUT_BF16, true, ACT_NONE>(p, acc, lds, row0, col0, lane, split);
+    epilogue<C, OUT, true, ACT_NONE>(p, acc, lds, row0, col0, lane, split);
   } else {
     const int act = p.act;
     if (act == ACT_NONE)
-      epilogue<C, OUT_BF16, false, ACT_NONE>(p, acc, lds, row0, col0, lane, split);
+      epilogue<C, OUT, false, ACT_NONE>(p, acc, lds, row0, col0, lane, split);
     else if (act == ACT_RELU)
-      epilogue<C, OUT_BF16, false, ACT_RELU>(p, acc, lds, row0, col0, lane, split);
+      epilogue<C, OUT, false, ACT_RELU>(p, acc, lds, row0, col0, lane, split);
     else if (act == ACT_GELU_ERF)
-      epilogue<C, OUT_BF16, false, ACT_GELU_ERF>(p, acc, lds, row0, col0, lane, split);
+      epilogue<C, OUT, false, ACT_GELU_ERF>(p, acc, lds, row0, col0, lane, split);
     else
-      epilogue<C, OUT_BF16, false, ACT_GELU_TANH>(p, acc, lds, row0, col0, lane, split);
+      epilogue<C, OUT, false, ACT_GELU_TANH>(p, acc, lds, row0, col0, lane, split);
   }
 }
 
 // ------------------------------------------------------------------- the kernel
 
-template <class C, int LA, int LB, bool OUT_BF16, bool SPLIT>
+template <class C, int LA, int LB, int OUT, bool SPLIT>
 __global__ void __launch_bounds__(C::NT)
 gemm_tile_kernel(GemmArgs p) {
   // The LDS block holds the ring of K slices, and after the main loop the
@@ -694,13 +690,13 @@ gemm_tile_kernel(GemmArgs p) {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   float* elds = reinterpret_cast<float*>(smem + wave * EpiLayout<C>::WAVE_BYTES);
   const int row0 = m0 + wm0, col0 = n0 + wn0;
-  run_epilogue<C, OUT_BF16, SPLIT>(p, acc, elds, row0, col0, lane, split);
+  run_epilogue<C, OUT, SPLIT>(p, acc, elds, row0, col0, lane, split);
 }
 
 // ----------------------------------------------------------- split-K reduction
 
 // C = epilogue(sum over splits s = 0..S-1, in that order, of workspace[s]).
-template <bool FP8, bool OUT_BF16>
+template <bool FP8, int OUT>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs p) {
   const int64_t MN = static_cast<int64_t>(p.M) * p.N;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -712,15 +708,14 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs p) {
   if constexpr (FP8) v = v * (p.scale_a[m] * p.scale_b[n]);
   v = p.alpha * v;
   const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
-  if (p.beta != 0.f) {
-    const float cin = OUT_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.C)[off])
-                               : static_cast<const float*>(p.C)[off];
-    v += p.beta * cin;
+  if constexpr (OUT == OUT_F32 || OUT == OUT_BF16) {
+    if (p.beta != 0.f) v += p.beta * load_cin1<OUT>(p.C, off);
   }
   if (p.bias) v += bf16_bits_to_f32(p.bias[n]);
   v = apply_act(v, p.act);
-  if constexpr (OUT_BF16) static_cast<uint16_t*>(p.C)[off] = f32_to_bf16_bits(v);
-  else static_cast<float*>(p.C)[off] = v;
+  float qs, qz;
+  out_row_params<OUT>(p, m, qs, qz);
+  store_out1<OUT>(p.C, off, v, qs, qz);
 }
 
 // ------------------------------------------------------------------- launchers
@@ -731,11 +726,15 @@ static hipError_t launch_cfg(const Plan& plan, const LaunchSpec& spec, const Gem
                              hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(plan.grid)), block(C::NT);
   if (plan.split > 1)
-    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, false, true>), grid, block, 0, stream, a);
-  else if (spec.out_bf16)
-    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, true, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_F32, true>), grid, block, 0, stream, a);
+  else if (spec.out == OUT_BF16)
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_BF16, false>), grid, block, 0, stream, a);
+  else if (spec.out == OUT_I8)
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_I8, false>), grid, block, 0, stream, a);
+  else if (spec.out == OUT_E4M3)
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_E4M3, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, false, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_F32, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -777,19 +776,25 @@ hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs&
                   : launch_cfg<Small16, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream);
 }
 
+template <bool FP8>
+static hipError_t launch_reduce(const LaunchSpec& spec, const GemmArgs& a, hipStream_t stream) {
+  const int64_t MN = static_cast<int64_t>(a.M) * a.N;
+  const dim3 grid(static_cast<unsigned>((MN + 255) / 256)), block(256);
+  if (spec.out == OUT_BF16)
+    hipLaunchKernelGGL((splitk_reduce_kernel<FP8, OUT_BF16>), grid, block, 0, stream, a);
+  else if (spec.out == OUT_I8)
+    hipLaunchKernelGGL((splitk_reduce_kernel<FP8, OUT_I8>), grid, block, 0, stream, a);
+  else if (spec.out == OUT_E4M3)
+    hipLaunchKernelGGL((splitk_reduce_kernel<FP8, OUT_E4M3>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<FP8, OUT_F32>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_splitk_reduce(const Plan& plan, const LaunchSpec& spec, const GemmArgs& a,
                                 hipStream_t stream) {
   (void)plan;
-  const int64_t MN = static_cast<int64_t>(a.M) * a.N;
-  const dim3 grid(static_cast<unsigned>((MN + 255) / 256)), block(256);
-  if (spec.fp8) {
-    if (spec.out_bf16) hipLaunchKernelGGL((splitk_reduce_kernel<true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((splitk_reduce_kernel<true, false>), grid, block, 0, stream, a);
-  } else {
-    if (spec.out_bf16) hipLaunchKernelGGL((splitk_reduce_kernel<false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((splitk_reduce_kernel<false, false>), grid, block, 0, stream, a);
-  }
-  return hipGetLastError();
+  return spec.fp8 ? launch_reduce<true>(spec, a, stream) : launch_reduce<false>(spec, a, stream);
 }
 
 #endif  // G355_KERNELS_ONLY

@@ -34,7 +34,7 @@ struct LaunchSpec {
   bool fp8;
   int loader_a, loader_b;  // Loader
   bool a_kmajor, b_kmajor; // layout of each operand (true = K contiguous)
-  bool out_bf16;
+  int out;                 // OutKind
 };
 
 // Enqueue the kernels of a plan. Returns the HIP error of the launch(es).

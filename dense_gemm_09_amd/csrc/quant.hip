@@ -37,19 +37,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Four float32 quotients -> four E4M3 codes in one 32-bit word (byte q holds
-// element q).
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  const float lim = 448.f;
-  a = __builtin_amdgcn_fmed3f(a, -lim, lim);
-  b = __builtin_amdgcn_fmed3f(b, -lim, lim);
-  c = __builtin_amdgcn_fmed3f(c, -lim, lim);
-  d = __builtin_amdgcn_fmed3f(d, -lim, lim);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return static_cast<uint32_t>(w);
-}
-
 __device__ __forceinline__ float amax8(float amax, const uint4& v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

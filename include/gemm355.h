@@ -105,6 +105,59 @@ gemm_status gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, float alpha,
                             const void* bias, gemm_act act,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Element type of a quantised output (gemm_*_quant). */
+typedef enum { GEMM_QOUT_INT8 = 0, GEMM_QOUT_E4M3 = 1 } gemm_qout_dtype;
+
+/*
+ * GEMM with a quantising epilogue: the FP32 epilogue value is quantised per
+ * token (row) and written as one byte per element, so the next layer reads a
+ * quarter of the FP32 bytes and no separate quantisation pass over C is
+ * needed (first DeepGEMM page, sec. 6.2: the quantisation
+ * round(x * scale + zero_point) applied to each output fragment inside the
+ * epilogue, with one scale per row looked up by the row index). For output
+ * element (m, n):
+ *
+ *   z = alpha * (scale_a[m] * scale_b[n]) * sum_k a(m,k) b(k,n) + bias[n]
+ *       (scale_a, scale_b only in gemm_fp8_scaled_quant)
+ *   y = act(z)                                     (FP32, as in gemm_bf16)
+ *   GEMM_QOUT_INT8: v = fp32(y * out_scale[m] + zp[m]) (fused multiply-add,
+ *                   one rounding; zp = out_zero[m], or 0 when out_zero is NULL)
+ *                   Q[m*ldq+n] = int8 of round-to-nearest-even(v), saturated
+ *                   to [-128, 127]
+ *   GEMM_QOUT_E4M3: w = fp32(y * out_scale[m])
+ *                   Q[m*ldq+n] = OCP E4M3FN code of w, round to nearest even,
+ *                   saturating at +-448 (out_zero must be NULL)
+ *
+ * out_scale multiplies (it is the inverse of the dequantisation step); the
+ * next layer recovers y ~ (q - zp) / out_scale. There is no beta and no C_in:
+ * Q is only written. A, B, layouts, bias, act, scale_a / scale_b, workspace
+ * and stream are as in gemm_bf16 / gemm_fp8_scaled (same layout rules, same
+ * workspace size query with is_fp8 = 0 / 1).
+ * Q: device, M x N bytes, row-major, ldq >= N (int8 or E4M3 codes).
+ * out_scale: device FP32[M], finite; out_zero: device INT32[M] with values of
+ * magnitude below 2^24, or NULL. NaN or infinite y give undefined codes.
+ * Errors (before anything is enqueued): GEMM_ERR_BAD_ENUM (q_dtype, layout
+ * or act), GEMM_ERR_UNSUPPORTED (out_zero given with GEMM_QOUT_E4M3, or a
+ * layout the dtype does not support), GEMM_ERR_NULL_POINTER (out_scale, Q,
+ * A / B when K > 0, the FP8 scales), and the other codes as for the plain calls.
+ */
+gemm_status gemm_bf16_quant(int64_t M, int64_t N, int64_t K, float alpha,
+                            const void* A, int64_t lda, gemm_layout layout_a,
+                            const void* B, int64_t ldb, gemm_layout layout_b,
+                            const void* bias, gemm_act act,
+                            const float* out_scale, const int32_t* out_zero,
+                            void* Q, int64_t ldq, gemm_qout_dtype q_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+gemm_status gemm_fp8_scaled_quant(int64_t M, int64_t N, int64_t K, float alpha,
+                                  const void* A, int64_t lda, gemm_layout layout_a,
+                                  const void* B, int64_t ldb, gemm_layout layout_b,
+                                  const float* scale_a, const float* scale_b,
+                                  const void* bias, gemm_act act,
+                                  const float* out_scale, const int32_t* out_zero,
+                                  void* Q, int64_t ldq, gemm_qout_dtype q_dtype,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Per-token FP8 quantisation of BF16 activations, producing the A operand and
  * scale_a of gemm_fp8_scaled (the per-token scaling of DeepGEMM: FP8 precision

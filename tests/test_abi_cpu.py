@@ -179,3 +179,38 @@ def test_quantizer_validation_before_launch():
     assert quant(Q=None) == NULLP
     # M == 0: nothing to do, no pointer is touched
     assert quant(M=0, X=None, Q=None, scale=None) == OK
+
+
+def qgemm(fp8_=False, M=64, N=64, K=64, A=FAKE, la=ROW, B=FAKE, lb=COL, sa=FAKE, sb=FAKE,
+          act=0, osc=FAKE, ozp=None, Q=FAKE, ldq=None, qd=g.QOUT_INT8, ws=None, wsb=0):
+    lda = K if la == ROW else M
+    ldb = N if lb == ROW else K
+    ldq = N if ldq is None else ldq
+    if fp8_:
+        return g.lib().gemm_fp8_scaled_quant(M, N, K, 1.0, A, lda, la, B, ldb, lb, sa, sb, None,
+                                             act, osc, ozp, Q, ldq, qd, ws, wsb, None)
+    return g.lib().gemm_bf16_quant(M, N, K, 1.0, A, lda, la, B, ldb, lb, None, act, osc, ozp, Q,
+                                   ldq, qd, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fp8_", [False, True])
+def test_quantising_gemm_validation_before_launch(fp8_):
+    assert qgemm(fp8_, qd=2) == BAD_ENUM
+    assert qgemm(fp8_, qd=-1) == BAD_ENUM
+    assert qgemm(fp8_, act=9) == BAD_ENUM
+    assert qgemm(fp8_, qd=g.QOUT_E4M3, ozp=FAKE) == UNSUP
+    assert qgemm(fp8_, osc=None) == NULLP
+    assert qgemm(fp8_, Q=None) == NULLP
+    assert qgemm(fp8_, ldq=63) == BAD_LD
+    assert qgemm(fp8_, M=-1) == BAD_DIM
+    if fp8_:
+        assert qgemm(True, sa=None) == NULLP
+        assert qgemm(True, lb=ROW) == UNSUP
+    # a split-K plan needs its workspace
+    ws = g.workspace_size(64, 4096, 4096, fp8_)
+    if ws:
+        assert qgemm(fp8_, M=64, N=4096, K=4096) == NULLP
+        assert qgemm(fp8_, M=64, N=4096, K=4096, ws=FAKE, wsb=ws - 1) == WS_SMALL
+    # M == 0 or N == 0: nothing is launched or read
+    assert qgemm(fp8_, M=0, A=None, B=None, osc=None, Q=None) == OK
+    assert qgemm(fp8_, N=0, ldq=1, A=None, B=None, osc=None, Q=None) == OK
