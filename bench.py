@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB device copy (counter "
                          "calibration) then 3 launches of each headline GEMM")
-    ap.add_argument("--only", default="", help="comma list of extra groups: decode,ffn,ragged,proj,quant,qout")
+    ap.add_argument("--only", default="", help="comma list of extra groups: decode,ffn,ragged,proj,quant,qout,mx")
     return ap.parse_args()
 
 
@@ -60,7 +60,7 @@ class Workload:
         for _ in range(copies - 1):
             self.sets.append({k: (v.clone() if v is not None else None) for k, v in base.items()})
         import dense_gemm_09_amd as g
-        need = g.workspace_size(p.M, p.N, p.K, p.kind == "fp8")
+        need = g.workspace_size(p.M, p.N, p.K, p.kind != "bf16")
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda") if need else None
         self.i = 0
 
@@ -247,7 +247,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extras:
-        only = set(args.only.split(",")) if args.only else {"decode", "ffn", "ragged", "proj", "quant", "qout"}
+        only = set(args.only.split(",")) if args.only else {"decode", "ffn", "ragged", "proj", "quant", "qout", "mx"}
         extra.update(run_extras(only))
 
     cpu = None
@@ -330,6 +330,13 @@ def run_extras(only):
             log(f"[bench] quant_fp8_rows_{M}x{K}: {r}")
             del xs, qs, ss
             torch.cuda.empty_cache()
+    if "mx" in only:
+        # MX FP8 (E8M0 scale per 32 K elements of each row of A / column of B)
+        # at 4096^3, BF16 out: the per-group variant of the FP8 GEMM.
+        import synth
+        p = synth.make_mx_problem(4096, 4096, 4096, seed_base=0x5EEDC000, c_dtype=synth.OUT_BF16,
+                                  a_std=1.0, b_std=4096 ** -0.5, name="mxfp8_4096^3")
+        measure("mxfp8_4096", p, steps=20, warmup=3)
     if "qout" in only:
         # The FP8 projection (4096 x 7168 x 2048, bias, GELU) with the
         # quantising epilogue: one byte per output element instead of BF16's

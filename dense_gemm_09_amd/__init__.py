@@ -26,7 +26,7 @@ ACT_NONE, ACT_RELU, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2, 3
 STATUS = ["GEMM_OK", "GEMM_ERR_NULL_POINTER", "GEMM_ERR_BAD_DIM", "GEMM_ERR_BAD_LD",
           "GEMM_ERR_BAD_ENUM", "GEMM_ERR_UNSUPPORTED", "GEMM_ERR_WORKSPACE_TOO_SMALL",
           "GEMM_ERR_HIP"]
-EXPORTS = ["gemm_bf16", "gemm_fp8_scaled", "gemm_bf16_quant", "gemm_fp8_scaled_quant",
+EXPORTS = ["gemm_bf16", "gemm_fp8_scaled", "gemm_mxfp8", "gemm_bf16_quant", "gemm_fp8_scaled_quant",
            "gemm_quantize_fp8_rows", "gemm_workspace_size", "gemm_plan", "gemm_status_string"]
 
 
@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
         L.gemm_fp8_scaled.restype = _I32
         L.gemm_fp8_scaled.argtypes = [_I64, _I64, _I64, _F32, _P, _I64, _I32, _P, _I64, _I32,
                                       _P, _P, _F32, _P, _I64, _I32, _P, _I32, _P, _SZ, _P]
+        L.gemm_mxfp8.restype = _I32
+        L.gemm_mxfp8.argtypes = [_I64, _I64, _I64, _F32, _P, _I64, _I32, _P, _I64, _I32, _P, _I64,
+                                 _P, _I64, _F32, _P, _I64, _I32, _P, _I32, _P, _SZ, _P]
         L.gemm_bf16_quant.restype = _I32
         L.gemm_bf16_quant.argtypes = [_I64, _I64, _I64, _F32, _P, _I64, _I32, _P, _I64, _I32,
                                       _P, _I32, _P, _P, _P, _I64, _I32, _P, _SZ, _P]
@@ -175,6 +178,24 @@ def gemm_fp8_scaled(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, scale_a,
                            _ptr(bias), act, _ptr(workspace), workspace_bytes, _stream(stream))
     if st != 0:
         raise GemmError(st, "gemm_fp8_scaled")
+
+
+def gemm_mxfp8(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, scale_a, ldsa, scale_b, ldsb,
+               beta, C, ldc, c_dtype, bias=None, act=ACT_NONE, workspace=None,
+               workspace_bytes=None, stream=None):
+    """C = act(alpha * sum_k a 2^(SA-127) b 2^(SB-127) + beta * C + bias): E4M3 with E8M0
+    scales per 32 K elements (scale_a: M rows of ldsa bytes, scale_b: N rows of ldsb)."""
+    L = lib()
+    _check_operands(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, c_dtype, 1, bias)
+    if M > 0 and N > 0 and K > 0:
+        _need(scale_a, M * ldsa, "scale_a")
+        _need(scale_b, N * ldsb, "scale_b")
+    workspace, workspace_bytes = _workspace(M, N, K, True, workspace, workspace_bytes, C)
+    st = L.gemm_mxfp8(M, N, K, alpha, _ptr(A), lda, layout_a, _ptr(B), ldb, layout_b,
+                      _ptr(scale_a), ldsa, _ptr(scale_b), ldsb, beta, _ptr(C), ldc, c_dtype,
+                      _ptr(bias), act, _ptr(workspace), workspace_bytes, _stream(stream))
+    if st != 0:
+        raise GemmError(st, "gemm_mxfp8")
 
 
 def _check_quant_out(M, N, Q, ldq, out_scale, out_zero):

@@ -115,13 +115,23 @@ bool valid_act(int a) { return a >= GEMM_ACT_NONE && a <= GEMM_ACT_GELU_TANH; }
 bool valid_qout(int q) { return q == GEMM_QOUT_INT8 || q == GEMM_QOUT_E4M3; }
 int qout_kind(int q) { return q == GEMM_QOUT_INT8 ? OUT_I8 : OUT_E4M3; }
 
+// E8M0 block scales of an MX FP8 call: one byte per 32 K elements, rows of ld bytes.
+struct MxScales {
+  const void* a;
+  int64_t lda;
+  const void* b;
+  int64_t ldb;
+};
+
 // out_kind: OutKind. The quantised kinds (INT8, E4M3) come with beta == 0,
 // the per-row output scale qscale and, for INT8 only, an optional zero point.
+// mx: block scales of an MX call (fp8 true, scale_a / scale_b unused), or null.
 gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const void* A,
                 int64_t lda, int layout_a, const void* B, int64_t ldb, int layout_b,
                 const float* scale_a, const float* scale_b, float beta, void* C, int64_t ldc,
                 int out_kind, const float* qscale, const int32_t* qzero, const void* bias,
-                int act, void* workspace, size_t workspace_bytes, void* stream) {
+                int act, void* workspace, size_t workspace_bytes, void* stream,
+                const MxScales* mx = nullptr) {
   // ---- enums and sizes
   if (!valid_layout(layout_a) || !valid_layout(layout_b) || !valid_act(act))
     return GEMM_ERR_BAD_ENUM;
@@ -137,11 +147,26 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   if (lda < std::max<int64_t>(1, need_lda) || ldb < std::max<int64_t>(1, need_ldb) ||
       ldc < std::max<int64_t>(1, N))
     return GEMM_ERR_BAD_LD;
+  if (mx) {
+    // A row of scales is read one 4-byte word (four blocks) per 128-element
+    // K slice: at least ceil(K/32) bytes, a multiple of 4.
+    const int64_t nblk = std::max<int64_t>(4, (K + 31) / 32);
+    if (mx->lda < nblk || mx->ldb < nblk || mx->lda % 4 != 0 || mx->ldb % 4 != 0)
+      return GEMM_ERR_BAD_LD;
+    // 32-bit byte offsets into the scale arrays, rows of a partial tile included.
+    if ((M + 256) * mx->lda >= (int64_t{1} << 31) || (N + 256) * mx->ldb >= (int64_t{1} << 31))
+      return GEMM_ERR_BAD_DIM;
+  }
   if (M == 0 || N == 0) return GEMM_OK;
   // ---- pointers
   if (C == nullptr) return GEMM_ERR_NULL_POINTER;
   if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL_POINTER;
-  if (fp8 && (scale_a == nullptr || scale_b == nullptr)) return GEMM_ERR_NULL_POINTER;
+  if (fp8 && !mx && (scale_a == nullptr || scale_b == nullptr)) return GEMM_ERR_NULL_POINTER;
+  if (mx && K > 0) {
+    if (mx->a == nullptr || mx->b == nullptr) return GEMM_ERR_NULL_POINTER;
+    if ((reinterpret_cast<uintptr_t>(mx->a) & 3u) || (reinterpret_cast<uintptr_t>(mx->b) & 3u))
+      return GEMM_ERR_UNSUPPORTED;
+  }
   if (quant_out && qscale == nullptr) return GEMM_ERR_NULL_POINTER;
 
   const Plan plan = make_plan(M, N, K, fp8);
@@ -160,6 +185,7 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   spec.a_kmajor = layout_a == GEMM_ROW_MAJOR;
   spec.b_kmajor = layout_b == GEMM_COL_MAJOR;
   spec.out = out_kind;
+  spec.mx = mx != nullptr;
   const bool k_ok = K % ce == 0;
   // The DMA loader addresses an operand with 32-bit byte offsets from its base
   // and marks chunks past K with an offset just beyond the operand's extent:
@@ -175,12 +201,15 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   if (K == 0) spec.loader_a = spec.loader_b = LOAD_DIRECT;  // nothing is loaded
 
   const bool direct = spec.loader_a == LOAD_DIRECT && spec.loader_b == LOAD_DIRECT;
-  Plan p = (plan.kernel == KERNEL_SKINNY && !direct) ? make_tile_plan(M, N, K, fp8) : plan;
+  // MX runs on the DMA-fed 256x128 / 128x128 tiles only (no skinny kernel).
+  if (mx && !direct) return GEMM_ERR_UNSUPPORTED;
+  Plan p = (plan.kernel == KERNEL_SKINNY && (!direct || mx)) ? make_tile_plan(M, N, K, fp8) : plan;
   if (p.kernel == KERNEL_TILE && !direct) {
     p.bm = 128;
     p.bn = 128;
     p.waves = 4;
   }
+  if (mx && p.bm == 256 && p.bn == 256) p.bn = 128;
   GemmArgs a{};
   a.A = A;
   a.B = B;
@@ -191,6 +220,12 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   a.workspace = static_cast<float*>(workspace);
   a.qscale = quant_out ? qscale : nullptr;
   a.qzero = out_kind == OUT_I8 ? qzero : nullptr;
+  if (mx) {
+    a.mx_a = static_cast<const uint8_t*>(mx->a);
+    a.mx_b = static_cast<const uint8_t*>(mx->b);
+    a.ldsa = static_cast<int>(mx->lda);
+    a.ldsb = static_cast<int>(mx->ldb);
+  }
   a.lda = lda;
   a.ldb = ldb;
   a.ldc = ldc;
@@ -243,6 +278,17 @@ gemm_status gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, float alpha, const 
   if (!valid_out(c_dtype)) return GEMM_ERR_BAD_ENUM;
   return run(true, M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, scale_a, scale_b, beta,
              C, ldc, c_dtype, nullptr, nullptr, bias, act, workspace, workspace_bytes, stream);
+}
+
+gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                       gemm_layout layout_a, const void* B, int64_t ldb, gemm_layout layout_b,
+                       const void* scale_a, int64_t ldsa, const void* scale_b, int64_t ldsb,
+                       float beta, void* C, int64_t ldc, gemm_out_dtype c_dtype, const void* bias,
+                       gemm_act act, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_out(c_dtype)) return GEMM_ERR_BAD_ENUM;
+  const MxScales mx{scale_a, ldsa, scale_b, ldsb};
+  return run(true, M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, nullptr, nullptr, beta, C,
+             ldc, c_dtype, nullptr, nullptr, bias, act, workspace, workspace_bytes, stream, &mx);
 }
 
 gemm_status gemm_bf16_quant(int64_t M, int64_t N, int64_t K, float alpha, const void* A,

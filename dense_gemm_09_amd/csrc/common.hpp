@@ -33,6 +33,9 @@ struct GemmArgs {
   float* workspace;       // split-K partials
   const float* qscale;    // FP32[M] output scale (quantised outputs)
   const int32_t* qzero;   // INT32[M] output zero point (INT8 output) or nullptr
+  const uint8_t* mx_a;    // E8M0 block scales of A: M rows of ldsa bytes (MX FP8 only)
+  const uint8_t* mx_b;    // E8M0 block scales of B: N rows of ldsb bytes
+  int ldsa, ldsb;         // bytes per row of mx_a / mx_b (multiples of 4)
   int64_t lda, ldb, ldc;
   int M, N, K;
   float alpha, beta;

@@ -33,6 +33,8 @@
 //   A and B fragments put the same K indices in the same register slots, so the
 //   result does not depend on how the hardware orders K inside one MFMA.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -53,12 +55,17 @@ __device__ __forceinline__ int swz(int r) {
   else return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
-template <int BM_, int BN_, int WM_, int WN_, bool FP8_, int ROWB_, int STAGES_, int SPREAD_ = 1>
+template <int BM_, int BN_, int WM_, int WN_, bool FP8_, int ROWB_, int STAGES_, int SPREAD_ = 1,
+          bool MX_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, ROWB = ROWB_, STAGES = STAGES_;
   // K-steps over which the global->LDS loads of one slice are issued.
   static constexpr int SPREAD = SPREAD_;
   static constexpr bool FP8 = FP8_;
+  // MX: FP8 with one E8M0 scale per 32 K elements of each row of A and column
+  // of B, applied by the MFMA itself (no FP32 per-row / per-column scales).
+  static constexpr bool MX = MX_;
+  static_assert(!MX || (FP8 && ROWB == 128), "MX scales: FP8 with four 32-element blocks per slice");
   static constexpr int NWAVES = WM * WN;
   static constexpr int NT = NWAVES * 64;
   static constexpr int ES = FP8 ? 1 : 2;      // bytes per element
@@ -332,7 +339,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (n + q < N) {
-        if constexpr (C::FP8) cs[q] = p.alpha * p.scale_b[n + q];
+        if constexpr (C::FP8 && !C::MX) cs[q] = p.alpha * p.scale_b[n + q];
         if (p.bias) bias_v[q] = bf16_bits_to_f32(p.bias[n + q]);
       }
     }
@@ -372,6 +379,35 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
     if (use_c) load_cin(0, cin[0]);
   }
 
+  // Per-row factors (scale_a for FP8, the output scale and zero point for
+  // quantised outputs) of the wave's 32*FM rows, loaded once up front: lane l
+  // holds rows l and 64 + l. A row's value is later taken from its lane with
+  // a cross-lane read, so no global load (and no wait on one, which on this
+  // chip would also wait for every earlier store) sits inside the row loop.
+  constexpr bool ROW_SA = !SPLIT && C::FP8 && !C::MX;
+  constexpr bool ROW_QS = !SPLIT && OUT >= OUT_I8;
+  constexpr bool ROW_QZ = !SPLIT && OUT == OUT_I8;
+  constexpr int RREG = (32 * C::FM + 63) / 64;
+  float row_sa[RREG], row_qs[RREG], row_qz[RREG];
+#pragma unroll
+  for (int j = 0; j < RREG; ++j) {
+    const int lr = 64 * j + lane;
+    const int m = row0 + lr;
+    const bool ok = lr < 32 * C::FM && m < M;
+    row_sa[j] = 1.f;
+    row_qs[j] = 1.f;
+    row_qz[j] = 0.f;
+    if constexpr (ROW_SA) {
+      if (ok) row_sa[j] = p.scale_a[m];
+    }
+    if constexpr (ROW_QS) {
+      if (ok) row_qs[j] = p.qscale[m];
+    }
+    if constexpr (ROW_QZ) {
+      if (ok && p.qzero) row_qz[j] = static_cast<float>(p.qzero[m]);
+    }
+  }
+
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
     if constexpr (HAS_CIN) {
@@ -389,6 +425,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
       const int r = it * E::RPI + rq;
       const int m = row0 + 32 * i + r;
       const float4 a4 = *reinterpret_cast<const float4*>(lds + r * E::STR + 4 * cq);
+      // Row m's factors sit in lane 32*(i&1) + r, register i/2. Read them
+      // while every lane is active: a cross-lane read from a lane that has
+      // left the loop below would not see its register.
+      const int src = 32 * (i & 1) + r;
+      float sa = 1.f, qs = 1.f, qz = 0.f;
+      if constexpr (ROW_SA) sa = __shfl(row_sa[i >> 1], src);
+      if constexpr (ROW_QS) qs = __shfl(row_qs[i >> 1], src);
+      if constexpr (ROW_QZ) qz = __shfl(row_qz[i >> 1], src);
       if (m >= M) continue;
       float v[4] = {a4.x, a4.y, a4.z, a4.w};
       if constexpr (SPLIT) {
@@ -402,8 +446,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
         }
         continue;
       } else {
-        if constexpr (C::FP8) {
-          const float sa = p.scale_a[m];
+        if constexpr (ROW_SA) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = fmaf(v[q], sa * cs[q], bias_v[q]);
         } else {
@@ -419,8 +462,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = apply_act(v[q], ACT);
-        float qs, qz;
-        out_row_params<OUT>(p, m, qs, qz);
         const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
         if (vec_ok) {
           store_out4<OUT>(p.C, off, v, qs, qz);
@@ -557,9 +598,17 @@ gemm_tile_kernel(GemmArgs p) {
       for (int j = 0; j < C::FN; ++j)
         fb[j] = *reinterpret_cast<const bf16x8*>(bt + b_row + j * 32 * C::ROWB + co);
     } else {
-      const int c0 = 4 * t + 2 * half;
+      // Registers 0-3 and 4-7 of a lane take two 16-byte chunks of its row.
+      // The MX scaled MFMA treats registers 0-3 of lanes i and i+32 as one
+      // 32-element K block (scaled by lane i's scale byte) and registers 4-7
+      // as the next (lane i+32's byte), so with MX the chunks are 4t+half and
+      // 4t+2+half: block 2t of the slice, then block 2t+1. Without block
+      // scales any assignment works as long as A and B agree; the plain path
+      // keeps a lane's 32 bytes contiguous.
+      const int c0 = C::MX ? 4 * t + half : 4 * t + 2 * half;
+      const int c1 = C::MX ? c0 + 2 : c0 + 1;
       const int co0 = (c0 ^ sw) << 4;
-      const int co1 = ((c0 + 1) ^ sw) << 4;
+      const int co1 = (c1 ^ sw) << 4;
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
         const i32x4 lo = *reinterpret_cast<const i32x4*>(at + a_row + i * 32 * C::ROWB + co0);
@@ -574,17 +623,38 @@ gemm_tile_kernel(GemmArgs p) {
       }
     }
   };
-  auto mfmas = [&](const Frag (&fa)[C::FM], const Frag (&fb)[C::FN]) {
+  // MX block scales of the slice being multiplied: per A row block i (B
+  // column block j) the word holding the four E8M0 scales of the lane's row
+  // (column) for this slice, shifted right by 8*half, so that byte 2t is the
+  // scale of the block k-step t takes from this lane (block 2t for lanes
+  // 0-31, 2t+1 for lanes 32-63).
+  constexpr int SFM = C::MX ? C::FM : 1, SFN = C::MX ? C::FN : 1;
+  uint32_t mxa[SFM], mxb[SFN];
+#pragma unroll
+  for (int i = 0; i < SFM; ++i) mxa[i] = 0x7f7f7f7fu;
+#pragma unroll
+  for (int j = 0; j < SFN; ++j) mxb[j] = 0x7f7f7f7fu;
+
+  auto mfmas_sel = [&](auto sel, const Frag (&fa)[C::FM], const Frag (&fb)[C::FN]) {
+    constexpr int S = decltype(sel)::value;  // byte of the scale words (2t)
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
-        if constexpr (C::FP8)
+        if constexpr (C::MX)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[i], fb[j], acc[i][j], 0, 0, S, static_cast<int>(mxa[i]), S,
+              static_cast<int>(mxb[j]));
+        else if constexpr (C::FP8)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0,
                                                                      0, 0, 127, 0, 127);
         else
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
+  };
+  auto mfmas = [&](const Frag (&fa)[C::FM], const Frag (&fb)[C::FN], int t) {
+    if (!C::MX || t == 0) mfmas_sel(std::integral_constant<int, 0>{}, fa, fb);
+    else mfmas_sel(std::integral_constant<int, 2>{}, fa, fb);
   };
 
   // The K loop is one stream of k-steps. Each k-step issues its MFMAs on the
@@ -628,6 +698,47 @@ gemm_tile_kernel(GemmArgs p) {
     Pt::issue(da, db, a_tile(st), b_tile(st), wave, rsrc_a, rsrc_b, ext_a, ext_b, k0 * C::ES, k0,
               k_end, k0 + C::BKE <= k_end);
   };
+  // ---- MX scale words. Every byte offset (row * ld + 4 * slice) is in the
+  // per-lane offset and checked against the array's extent by the buffer
+  // descriptor: rows past M (N) and words past the end read zeros.
+  uint32_t mxa_raw[SFM], mxb_raw[SFN];
+  // (Unused, and removed by the compiler, on the other paths.)
+  const __amdgpu_buffer_rsrc_t rsrc_sa = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.mx_a), 0, C::MX ? p.M * p.ldsa : 0, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsrc_sb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.mx_b), 0, C::MX ? p.N * p.ldsb : 0, kBufferWord3);
+  uint32_t voff_sa = 0, voff_sb = 0;
+  int mx_blocks = 0;
+  if constexpr (C::MX) {
+    voff_sa = static_cast<uint32_t>(m0 + wm0 + (lane & 31)) * static_cast<uint32_t>(p.ldsa);
+    voff_sb = static_cast<uint32_t>(n0 + wn0 + (lane & 31)) * static_cast<uint32_t>(p.ldsb);
+    mx_blocks = (p.K + 31) >> 5;
+  }
+  // Issue the scale-word loads of slice s.
+  auto mx_load = [&](int s) __attribute__((always_inline)) {
+    const uint32_t kb = static_cast<uint32_t>((k_begin + s * C::BKE) >> 5);
+#pragma unroll
+    for (int i = 0; i < SFM; ++i)
+      mxa_raw[i] = __builtin_amdgcn_raw_buffer_load_b32(
+          rsrc_sa, voff_sa + static_cast<uint32_t>(32 * i * p.ldsa) + kb, 0, 0);
+#pragma unroll
+    for (int j = 0; j < SFN; ++j)
+      mxb_raw[j] = __builtin_amdgcn_raw_buffer_load_b32(
+          rsrc_sb, voff_sb + static_cast<uint32_t>(32 * j * p.ldsb) + kb, 0, 0);
+  };
+  // Make slice s's loaded words current: blocks at or past ceil(K/32) get the
+  // neutral scale 127 (their data are zeros, and a NaN scale code in the
+  // caller's padding must not turn them into NaN), then the per-half shift.
+  auto mx_ready = [&](int s) __attribute__((always_inline)) {
+    const int rem = mx_blocks - ((k_begin + s * C::BKE) >> 5);
+    const uint32_t keep = rem >= 4 ? 0xffffffffu : rem <= 0 ? 0u : (0xffffffffu >> (8 * (4 - rem)));
+    const uint32_t fill = 0x7f7f7f7fu & ~keep;
+#pragma unroll
+    for (int i = 0; i < SFM; ++i) mxa[i] = ((mxa_raw[i] & keep) | fill) >> (8 * half);
+#pragma unroll
+    for (int j = 0; j < SFN; ++j) mxb[j] = ((mxb_raw[j] & keep) | fill) >> (8 * half);
+  };
+
   auto boundary = [&](int j) {
     commit((j + C::STAGES - 1) % C::STAGES);
     wait_loads_and_barrier<DMA_BEHIND>();
@@ -639,7 +750,8 @@ gemm_tile_kernel(GemmArgs p) {
     if (t == C::KSTEPS - 1) {
       boundary(j);
       reads((j + 1) % C::STAGES, 0, na, nb);
-      mfmas(ca, cb);
+      mfmas(ca, cb, t);
+      if constexpr (C::MX) mx_ready(j + 1);
       step_hint<READS, MFMAS, ALL_DMA ? Part0::COUNT : 0>();
     } else {
       // Later parts of the loads of slice j-1+STAGES.
@@ -648,8 +760,11 @@ gemm_tile_kernel(GemmArgs p) {
         if (t == 1) dma_part(Part2{}, j - 1 + C::STAGES);
         if (t == 2) dma_part(Part3{}, j - 1 + C::STAGES);
       }
+      if constexpr (C::MX) {
+        if (t == 0) mx_load(j + 1);
+      }
       reads(j % C::STAGES, t + 1, na, nb);
-      mfmas(ca, cb);
+      mfmas(ca, cb, t);
       if (t == 0) step_hint<READS, MFMAS, ALL_DMA ? Part1::COUNT : 0>();
       else if (t == 1) step_hint<READS, MFMAS, ALL_DMA ? Part2::COUNT : 0>();
       else if (t == 2) step_hint<READS, MFMAS, ALL_DMA ? Part3::COUNT : 0>();
@@ -665,7 +780,9 @@ gemm_tile_kernel(GemmArgs p) {
       fetch(s, k_begin + s * C::BKE);
       commit(s);
     }
+    if constexpr (C::MX) mx_load(0);
     wait_loads_and_barrier<DMA_BEHIND>();
+    if constexpr (C::MX) mx_ready(0);
     fetch(C::STAGES - 1, k_begin + (C::STAGES - 1) * C::BKE);
     reads(0, 0, fa0, fb0);
     // Slices are taken U at a time so that each loop iteration holds an even
@@ -721,20 +838,27 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs p) {
 // ------------------------------------------------------------------- launchers
 #ifndef G355_KERNELS_ONLY
 
-template <class C, int LA, int LB>
+template <class C, int LA, int LB, bool QUANT_OUT = true>
 static hipError_t launch_cfg(const Plan& plan, const LaunchSpec& spec, const GemmArgs& a,
                              hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(plan.grid)), block(C::NT);
-  if (plan.split > 1)
+  if (plan.split > 1) {
     hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_F32, true>), grid, block, 0, stream, a);
-  else if (spec.out == OUT_BF16)
+  } else if (spec.out == OUT_BF16) {
     hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_BF16, false>), grid, block, 0, stream, a);
-  else if (spec.out == OUT_I8)
-    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_I8, false>), grid, block, 0, stream, a);
-  else if (spec.out == OUT_E4M3)
-    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_E4M3, false>), grid, block, 0, stream, a);
-  else
+  } else if (spec.out == OUT_I8 || spec.out == OUT_E4M3) {
+    if constexpr (QUANT_OUT) {
+      if (spec.out == OUT_I8)
+        hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_I8, false>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_E4M3, false>), grid, block, 0, stream,
+                           a);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else {
     hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_F32, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -750,6 +874,11 @@ using Mid16 = TileCfg<256, 128, 4, 2, false, 128, 2, 2>;
 using Mid8 = TileCfg<256, 128, 4, 2, true, 128, 2, 2>;
 using Small16 = TileCfg<128, 128, 2, 2, false, 128, 2>;
 using Small8 = TileCfg<128, 128, 2, 2, true, 128, 2>;
+// MX (E8M0 block-scaled) FP8: the scale words take up to 12 more VGPRs per
+// lane, which the 256x256 FP8 tile (at the 256-register limit) does not have;
+// its plans run on 256x128.
+using Mid8X = TileCfg<256, 128, 4, 2, true, 128, 2, 2, true>;
+using Small8X = TileCfg<128, 128, 2, 2, true, 128, 2, 1, true>;
 
 hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
                        hipStream_t stream) {
@@ -757,6 +886,13 @@ hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs&
   a.a_mn_major = spec.a_kmajor ? 0 : 1;
   a.b_mn_major = spec.b_kmajor ? 0 : 1;
   const bool direct = spec.loader_a == LOAD_DIRECT && spec.loader_b == LOAD_DIRECT;
+  if (spec.mx) {
+    // MX operands take the DMA loader only (checked by the caller).
+    if (!direct) return hipErrorInvalidValue;
+    if (plan.bm == 256)
+      return launch_cfg<Mid8X, LOAD_DIRECT, LOAD_DIRECT, false>(plan, spec, a, stream);
+    return launch_cfg<Small8X, LOAD_DIRECT, LOAD_DIRECT, false>(plan, spec, a, stream);
+  }
   if (!direct) {
     // Register loading runs on the 128x128 tile only.
     if (spec.fp8) return launch_cfg<Small8, LOAD_GENERIC, LOAD_GENERIC>(plan, spec, a, stream);
@@ -794,7 +930,10 @@ static hipError_t launch_reduce(const LaunchSpec& spec, const GemmArgs& a, hipSt
 hipError_t launch_splitk_reduce(const Plan& plan, const LaunchSpec& spec, const GemmArgs& a,
                                 hipStream_t stream) {
   (void)plan;
-  return spec.fp8 ? launch_reduce<true>(spec, a, stream) : launch_reduce<false>(spec, a, stream);
+  // The FP32 per-row / per-column scales belong to plain FP8; MX scales were
+  // applied inside the MFMAs.
+  return spec.fp8 && !spec.mx ? launch_reduce<true>(spec, a, stream)
+                              : launch_reduce<false>(spec, a, stream);
 }
 
 #endif  // G355_KERNELS_ONLY

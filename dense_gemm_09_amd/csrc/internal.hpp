@@ -35,6 +35,7 @@ struct LaunchSpec {
   int loader_a, loader_b;  // Loader
   bool a_kmajor, b_kmajor; // layout of each operand (true = K contiguous)
   int out;                 // OutKind
+  bool mx;                 // FP8 with E8M0 block scales (GemmArgs::mx_a / mx_b)
 };
 
 // Enqueue the kernels of a plan. Returns the HIP error of the launch(es).

@@ -105,6 +105,40 @@ gemm_status gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, float alpha,
                             const void* bias, gemm_act act,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * MX FP8 GEMM: E4M3 x E4M3 with one power-of-two (E8M0) scale per 32
+ * consecutive K elements of each row of A and of each column of B, i.e. the
+ * per-group scaling the FP8 DeepGEMM page (sec. 3.2) names next to the
+ * per-token x per-channel form, in the block layout of the OCP
+ * Microscaling (MX) formats, which gfx950's scaled MFMA applies in hardware:
+ *
+ *   C = act( alpha * sum_k a(m,k) 2^(SA[m][k/32]-127) * b(k,n) 2^(SB[n][k/32]-127)
+ *            + beta * C + bias[n] )
+ *
+ * A: E4M3 codes, ROW (K-major), lda >= K. B: E4M3 codes, COL (K-major, N rows
+ * of ldb), ldb >= K. Other layouts: GEMM_ERR_UNSUPPORTED.
+ * scale_a: E8M0 codes (uint8), M rows of ldsa bytes; byte k/32 of row m
+ * scales a(m, k). scale_b: N rows of ldsb bytes; byte k/32 of row n scales
+ * b(k, n). Code c means 2^(c-127); code 255 (NaN) gives undefined results.
+ * ldsa, ldsb: >= ceil(K/32), multiples of 4, >= 4; the arrays must span
+ * M * ldsa and N * ldsb bytes, 4-byte aligned. Bytes past ceil(K/32) in a
+ * row are never used.
+ * A, B: rows 16-byte aligned (base and ld multiples of 16) and K a multiple of
+ * 16, otherwise GEMM_ERR_UNSUPPORTED (the path reads its operands by DMA only).
+ * There are no FP32 per-token / per-channel scales on this call. Epilogue,
+ * C, bias, act, beta, workspace (size: gemm_workspace_size(M, N, K, 1)) and
+ * stream as for gemm_fp8_scaled. Errors as for gemm_fp8_scaled, plus
+ * GEMM_ERR_BAD_LD for ldsa / ldsb, GEMM_ERR_NULL_POINTER for NULL scales when
+ * K > 0, GEMM_ERR_BAD_DIM when (M + 256) * ldsa or (N + 256) * ldsb reaches 2^31.
+ */
+gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K, float alpha,
+                       const void* A, int64_t lda, gemm_layout layout_a,
+                       const void* B, int64_t ldb, gemm_layout layout_b,
+                       const void* scale_a, int64_t ldsa, const void* scale_b, int64_t ldsb,
+                       float beta, void* C, int64_t ldc, gemm_out_dtype c_dtype,
+                       const void* bias, gemm_act act,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Element type of a quantised output (gemm_*_quant). */
 typedef enum { GEMM_QOUT_INT8 = 0, GEMM_QOUT_E4M3 = 1 } gemm_qout_dtype;
 

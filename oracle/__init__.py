@@ -24,16 +24,19 @@ tutorial page, sec. 6).
 The per-token FP8 quantiser that produces the FP8 GEMM's A operand (one
 float32 scale amax/448 per row, E4M3 codes of x / scale) is in quant.py; the
 quantising epilogue (per-row INT8 round(x * scale + zero_point) or E4M3 codes
-of x * scale, first DeepGEMM page, sec. 6.2) is in qout.py.
+of x * scale, first DeepGEMM page, sec. 6.2) is in qout.py; the block-scaled
+(MX, one E8M0 scale per 32 K elements) FP8 GEMM is in mx.py.
 
 Parity status: every function here is pinned by the `-m "not gpu"` tests in
-tests/test_oracle.py, tests/test_oracle_quant.py and tests/test_oracle_qout.py (codec tables, rounding ties, integer-valued exact
+tests/test_oracle.py, tests/test_oracle_quant.py, tests/test_oracle_qout.py and
+tests/test_oracle_mx.py (codec tables, rounding ties, integer-valued exact
 products, identity and permutation matrices, closed forms, linearity, GELU
 against tabulated normal-CDF values). No function is "parity unpinned".
 """
 from .codecs import (decode_bf16, decode_e4m3, round_to_bf16, round_to_bf16_bits,
                      round_to_f32)
 from .gemm import activation, gemm_bf16, gemm_fp8_scaled, logical_a, logical_b
+from .mx import decode_e8m0, gemm_mxfp8
 from .qout import QOUT_E4M3, QOUT_INT8, quantize_output
 from .quant import encode_e4m3, quantize_rows_e4m3
 
@@ -41,4 +44,5 @@ __all__ = [
     "decode_bf16", "decode_e4m3", "round_to_bf16", "round_to_bf16_bits", "round_to_f32",
     "activation", "gemm_bf16", "gemm_fp8_scaled", "logical_a", "logical_b",
     "encode_e4m3", "quantize_rows_e4m3", "quantize_output", "QOUT_INT8", "QOUT_E4M3",
+    "decode_e8m0", "gemm_mxfp8",
 ]

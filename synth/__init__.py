@@ -85,6 +85,90 @@ def quantize_rows_e4m3(x: np.ndarray):
     return q.view(torch.uint8).numpy().copy(), scale.numpy().copy()
 
 
+MX_BLOCK = 32
+E4M3_EMAX = 8            # exponent of E4M3's largest normal value (448 = 1.75 * 2^8)
+E8M0_NAN_BITS = np.uint8(0xFF)
+
+
+def mx_quantize_rows(x: np.ndarray):
+    """OCP Microscaling (MX) quantisation of each row in blocks of 32 elements.
+
+    Per block: shared exponent e = floor(log2(amax)) - 8 (0 for an all-zero
+    block), clamped to [-127, 127]; E8M0 code e + 127; elements are the E4M3
+    codes of x / 2^e, saturating at +-448. Returns (codes uint8 [R, K], scale
+    codes uint8 [R, ceil(K/32)]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    R, K = x.shape
+    nb = (K + MX_BLOCK - 1) // MX_BLOCK
+    padded = np.zeros((R, nb * MX_BLOCK))
+    padded[:, :K] = x
+    blocks = padded.reshape(R, nb, MX_BLOCK)
+    amax = np.abs(blocks).max(axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - E4M3_EMAX, 0.0)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    scaled = blocks / np.ldexp(1.0, e)[:, :, None]
+    codes = to_e4m3_bits(scaled.reshape(R, nb * MX_BLOCK)[:, :K])
+    return codes, (e + 127).astype(np.uint8)
+
+
+def mx_scale_ld(K: int) -> int:
+    """Smallest valid scale-row length: ceil(K/32) rounded up to a multiple of 4 (>= 4)."""
+    nb = (K + MX_BLOCK - 1) // MX_BLOCK
+    return max(4, (nb + 3) // 4 * 4)
+
+
+def make_mx_problem(M: int, N: int, K: int, *, seed_base: int, alpha: float = 1.0,
+                    beta: float = 0.0, lda: Optional[int] = None, ldb: Optional[int] = None,
+                    ldc: Optional[int] = None, ldsa: Optional[int] = None,
+                    ldsb: Optional[int] = None, c_dtype: int = OUT_F32, act: int = ACT_NONE,
+                    a_std: float = 1.0, b_std: float = 1.0, cin_std: float = 1.0,
+                    bias_std: Optional[float] = None, int_data: Optional[tuple] = None,
+                    scale_codes: Optional[tuple] = None, name: str = "") -> "Problem":
+    """An MX FP8 problem: A ROW (M x lda), B COL (N x ldb), E8M0 scales per 32 K.
+
+    Normal data are MX-quantised per row of A and per column of B. With
+    int_data=(lo, hi) the elements are small integers (exact in E4M3) and the
+    scale codes are drawn uniformly from scale_codes=(lo, hi). Scale bytes past
+    ceil(K/32) in a row hold the NaN code 0xFF (they must never be used).
+    """
+    lda = max(1, K) if lda is None else lda
+    ldb = max(1, K) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    ldsa = mx_scale_ld(K) if ldsa is None else ldsa
+    ldsb = mx_scale_ld(K) if ldsb is None else ldsb
+    nb = (K + MX_BLOCK - 1) // MX_BLOCK
+    if int_data is not None:
+        a_codes = to_e4m3_bits(small_ints((M, K), int_data[0], int_data[1], seed_base + 0))
+        bt_codes = to_e4m3_bits(small_ints((N, K), int_data[0], int_data[1], seed_base + 1))
+        lo, hi = scale_codes if scale_codes is not None else (127, 127)
+        rng = np.random.Generator(np.random.PCG64(seed_base + 5))
+        sa = rng.integers(lo, hi + 1, size=(M, nb)).astype(np.uint8)
+        sb = rng.integers(lo, hi + 1, size=(N, nb)).astype(np.uint8)
+    else:
+        a_codes, sa = mx_quantize_rows(normal((M, K), a_std, seed_base + 0))
+        bt_codes, sb = mx_quantize_rows(normal((K, N), b_std, seed_base + 1).T)
+    A = _pad(a_codes, lda, E4M3_NAN_BITS)
+    B = _pad(bt_codes, ldb, E4M3_NAN_BITS)
+    mx_a = np.full((M, ldsa), E8M0_NAN_BITS, np.uint8)
+    mx_a[:, :nb] = sa
+    mx_b = np.full((N, ldsb), E8M0_NAN_BITS, np.uint8)
+    mx_b[:, :nb] = sb
+    cin = normal((M, N), cin_std, seed_base + 2)
+    if c_dtype == OUT_F32:
+        C = np.full((M, ldc), np.nan, dtype=np.float32)
+        C[:, :N] = cin.astype(np.float32)
+    else:
+        C = np.full((M, ldc), BF16_NAN_BITS, dtype=np.uint16)
+        C[:, :N] = to_bf16_bits(cin)
+    bias = None
+    if bias_std is not None:
+        bias = to_bf16_bits(normal((N,), bias_std, seed_base + 3))
+    return Problem("mxfp8", M, N, K, alpha, beta, ROW, COL, lda, ldb, ldc, c_dtype, act, A, B, C,
+                   bias, None, None, name or f"mxfp8_{M}x{N}x{K}", mx_a, mx_b, ldsa, ldsb)
+
+
 def _pad(bits: np.ndarray, ld: int, pad_value) -> np.ndarray:
     rows, cols = bits.shape
     if ld == cols:
@@ -130,6 +214,11 @@ class Problem:
     scale_a: Optional[np.ndarray] = None  # float32 [M] (fp8 only)
     scale_b: Optional[np.ndarray] = None  # float32 [N] (fp8 only)
     name: str = ""
+    # MX FP8 (kind "mxfp8"): E8M0 block-scale codes, one per 32 K elements.
+    mx_a: Optional[np.ndarray] = None     # uint8 [M, ldsa]
+    mx_b: Optional[np.ndarray] = None     # uint8 [N, ldsb]
+    ldsa: int = 0
+    ldsb: int = 0
 
     @property
     def flops(self) -> int:

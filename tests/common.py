@@ -12,6 +12,9 @@ def reference(p, rows=None, cols=None):
     if p.kind == "bf16":
         return oracle.gemm_bf16(p.M, p.N, p.K, p.alpha, p.A, p.layout_a, p.B, p.layout_b,
                                 p.beta, p.C, p.c_dtype, p.bias, p.act, rows=rows, cols=cols)
+    if p.kind == "mxfp8":
+        return oracle.gemm_mxfp8(p.M, p.N, p.K, p.alpha, p.A, p.B, p.mx_a, p.mx_b, p.beta, p.C,
+                                 p.c_dtype, p.bias, p.act, rows=rows, cols=cols)
     return oracle.gemm_fp8_scaled(p.M, p.N, p.K, p.alpha, p.A, p.layout_a, p.B, p.layout_b,
                                   p.scale_a, p.scale_b, p.beta, p.C, p.c_dtype, p.bias, p.act,
                                   rows=rows, cols=cols)
@@ -24,6 +27,10 @@ def operand_norms(p, rows=None, cols=None):
     c = np.arange(p.N) if cols is None else np.asarray(cols)
     a = dec(oracle.logical_a(p.A, p.layout_a, p.M, p.K)[r, :])
     b = dec(oracle.logical_b(p.B, p.layout_b, p.K, p.N)[:, c])
+    if p.kind == "mxfp8" and p.K > 0:
+        kb = np.arange(p.K) // 32
+        a = a * oracle.decode_e8m0(np.asarray(p.mx_a)[r][:, kb])
+        b = b * oracle.decode_e8m0(np.asarray(p.mx_b)[c][:, kb]).T
     rn = np.sqrt((a * a).sum(axis=1))
     cn = np.sqrt((b * b).sum(axis=0))
     if p.kind == "fp8":

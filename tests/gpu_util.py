@@ -19,7 +19,8 @@ def to_device(p):
     import torch
     return dict(A=_dev(p.A, torch), B=_dev(p.B, torch), C=_dev(p.C, torch),
                 bias=_dev(p.bias, torch),
-                scale_a=_dev(p.scale_a, torch), scale_b=_dev(p.scale_b, torch))
+                scale_a=_dev(p.scale_a, torch), scale_b=_dev(p.scale_b, torch),
+                mx_a=_dev(p.mx_a, torch), mx_b=_dev(p.mx_b, torch))
 
 
 def call(p, d, workspace=None, stream=None):
@@ -28,6 +29,10 @@ def call(p, d, workspace=None, stream=None):
         g.gemm_bf16(p.M, p.N, p.K, p.alpha, d["A"], p.lda, p.layout_a, d["B"], p.ldb, p.layout_b,
                     p.beta, d["C"], p.ldc, p.c_dtype, d["bias"], p.act, workspace=workspace,
                     stream=stream)
+    elif p.kind == "mxfp8":
+        g.gemm_mxfp8(p.M, p.N, p.K, p.alpha, d["A"], p.lda, p.layout_a, d["B"], p.ldb, p.layout_b,
+                     d["mx_a"], p.ldsa, d["mx_b"], p.ldsb, p.beta, d["C"], p.ldc, p.c_dtype,
+                     d["bias"], p.act, workspace=workspace, stream=stream)
     else:
         g.gemm_fp8_scaled(p.M, p.N, p.K, p.alpha, d["A"], p.lda, p.layout_a, d["B"], p.ldb,
                           p.layout_b, d["scale_a"], d["scale_b"], p.beta, d["C"], p.ldc,

@@ -214,3 +214,34 @@ def test_quantising_gemm_validation_before_launch(fp8_):
     # M == 0 or N == 0: nothing is launched or read
     assert qgemm(fp8_, M=0, A=None, B=None, osc=None, Q=None) == OK
     assert qgemm(fp8_, N=0, ldq=1, A=None, B=None, osc=None, Q=None) == OK
+
+
+def mx(M=64, N=64, K=256, A=FAKE, lda=None, la=ROW, B=FAKE, ldb=None, lb=COL, sa=FAKE, ldsa=8,
+       sb=FAKE, ldsb=8, C=FAKE, ldc=None, cd=OUT_BF16, act=0, ws=None, wsb=0):
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return g.lib().gemm_mxfp8(M, N, K, 1.0, A, lda, la, B, ldb, lb, sa, ldsa, sb, ldsb, 0.0, C,
+                              ldc, cd, None, act, ws, wsb, None)
+
+
+def test_mx_validation_before_launch():
+    assert mx(cd=2) == BAD_ENUM
+    assert mx(act=7) == BAD_ENUM
+    assert mx(la=COL) == UNSUP
+    assert mx(lb=ROW) == UNSUP
+    assert mx(ldsa=7) == BAD_LD            # ceil(256/32) = 8 blocks
+    assert mx(ldsb=6) == BAD_LD
+    assert mx(ldsa=10) == BAD_LD           # not a multiple of 4
+    assert mx(K=32, ldsa=2, ldsb=4) == BAD_LD   # at least 4 bytes per row
+    assert mx(sa=None) == NULLP
+    assert mx(sb=None) == NULLP
+    assert mx(sa=FAKE + 2) == UNSUP        # scale rows must be 4-byte aligned
+    assert mx(A=FAKE + 8) == UNSUP         # operands are read by DMA only
+    assert mx(lda=264) == UNSUP            # 264 bytes: rows not 16-byte aligned... (264 % 16 = 8)
+    assert mx(M=1 << 24, ldsa=1 << 8) == BAD_DIM   # scale offsets past 2^31
+    assert mx(M=0, A=None, B=None, sa=None, sb=None) == OK
+    ws = g.workspace_size(64, 4096, 2048, True)
+    assert ws > 0
+    assert mx(N=4096, K=2048, ldsa=64, ldsb=64) == NULLP
+    assert mx(N=4096, K=2048, ldsa=64, ldsb=64, ws=FAKE, wsb=ws - 1) == WS_SMALL
