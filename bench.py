@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB device copy (counter "
                          "calibration) then 3 launches of each headline GEMM")
-    ap.add_argument("--only", default="", help="comma list of extra groups: decode,ffn,ragged,proj,quant,qout,mx")
+    ap.add_argument("--only", default="", help="comma list of extra groups: decode,ffn,ragged,proj,quant,qout,mx,pack")
     return ap.parse_args()
 
 
@@ -247,7 +247,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extras:
-        only = set(args.only.split(",")) if args.only else {"decode", "ffn", "ragged", "proj", "quant", "qout", "mx"}
+        only = set(args.only.split(",")) if args.only else {"decode", "ffn", "ragged", "proj", "quant", "qout", "mx", "pack"}
         extra.update(run_extras(only))
 
     cpu = None
@@ -337,6 +337,58 @@ def run_extras(only):
         p = synth.make_mx_problem(4096, 4096, 4096, seed_base=0x5EEDC000, c_dtype=synth.OUT_BF16,
                                   a_std=1.0, b_std=4096 ** -0.5, name="mxfp8_4096^3")
         measure("mxfp8_4096", p, steps=20, warmup=3)
+    if "pack" in only:
+        # Pre-laid-out weights: BF16 4096^3 with B row-major (N contiguous), as
+        # called directly (register loader) and after one gemm_pack_b into
+        # K-major rows (DMA path); and a fused projection (three 4096-column
+        # weights concatenated along N) as one launch vs three.
+        import dense_gemm_09_amd as g
+        from synth import make_problem, ROW, COL, OUT_BF16, OUT_F32
+        p = make_problem("bf16", 4096, 4096, 4096, seed_base=0x5EEDD200, layout_b=ROW,
+                         c_dtype=OUT_F32, a_std=4096 ** -0.5, b_std=4096 ** -0.5,
+                         name="bf16_4096^3_rowB")
+        measure("bf16_4096_rowB_direct", p, steps=5, warmup=2)
+        w = Workload(p, 1)
+        d = w.sets[0]
+        Bp = torch.empty((4096, 4096), dtype=torch.int16, device="cuda")
+
+        def do_pack():
+            g.pack_b(4096, 4096, d["B"], 4096, ROW, 2, Bp, 4096)
+
+        per, _, _ = time_calls([do_pack], 20, 3)
+        res["pack_b_bf16_4096x4096"] = {"us": round(per[0] * 1e3, 2),
+                                        "gbps": round(2 * 2 * 4096 * 4096 / (per[0] * 1e-3) / 1e9, 0)}
+        log(f"[bench] pack_b_bf16_4096x4096: {res['pack_b_bf16_4096x4096']}")
+        import copy
+        q = copy.copy(p)
+        q.layout_b, q.ldb = COL, 4096
+        q.B = Bp.cpu().numpy().view(np.uint16)
+        q.name = "bf16_4096^3_packedB"
+        del w
+        measure("bf16_4096_packedB", q, steps=10, warmup=3)
+        M, K, NS = 512, 4096, 4096
+        fused = make_problem("bf16", M, 3 * NS, K, seed_base=0x5EEDD300, layout_b=COL,
+                             c_dtype=OUT_BF16, a_std=1.0, b_std=0.02, name="proj_fused")
+        wf = Workload(fused, copies_for(fused))
+        per_f, _, _ = time_calls([wf], 20, 3)
+        sets = wf.sets
+        Cs = [torch.empty((M, NS), dtype=torch.int16, device="cuda") for _ in range(3)]
+        ws = torch.empty(max(1, g.workspace_size(M, NS, K, False)), dtype=torch.uint8, device="cuda")
+        st = {"i": 0}
+
+        def three():
+            dd = sets[st["i"] % len(sets)]
+            st["i"] += 1
+            for j in range(3):
+                g.gemm_bf16(M, NS, K, 1.0, dd["A"], K, ROW, dd["B"][j * NS:(j + 1) * NS], K, COL,
+                            0.0, Cs[j], NS, OUT_BF16, workspace=ws)
+
+        per_3, _, _ = time_calls([three], 20, 3)
+        res["proj_512x3x4096x4096"] = {"fused_us": round(per_f[0] * 1e3, 2),
+                                       "three_launches_us": round(per_3[0] * 1e3, 2)}
+        log(f"[bench] proj_512x3x4096x4096: {res['proj_512x3x4096x4096']}")
+        del wf, sets, Cs
+        torch.cuda.empty_cache()
     if "qout" in only:
         # The FP8 projection (4096 x 7168 x 2048, bias, GELU) with the
         # quantising epilogue: one byte per output element instead of BF16's

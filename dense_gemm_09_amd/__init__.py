@@ -27,7 +27,8 @@ STATUS = ["GEMM_OK", "GEMM_ERR_NULL_POINTER", "GEMM_ERR_BAD_DIM", "GEMM_ERR_BAD_
           "GEMM_ERR_BAD_ENUM", "GEMM_ERR_UNSUPPORTED", "GEMM_ERR_WORKSPACE_TOO_SMALL",
           "GEMM_ERR_HIP"]
 EXPORTS = ["gemm_bf16", "gemm_fp8_scaled", "gemm_mxfp8", "gemm_bf16_quant", "gemm_fp8_scaled_quant",
-           "gemm_quantize_fp8_rows", "gemm_workspace_size", "gemm_plan", "gemm_status_string"]
+           "gemm_quantize_fp8_rows", "gemm_pack_b", "gemm_workspace_size", "gemm_plan",
+           "gemm_status_string"]
 
 
 class GemmError(RuntimeError):
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_fp8_scaled_quant.argtypes = [_I64, _I64, _I64, _F32, _P, _I64, _I32, _P, _I64,
                                             _I32, _P, _P, _P, _I32, _P, _P, _P, _I64, _I32, _P,
                                             _SZ, _P]
+        L.gemm_pack_b.restype = _I32
+        L.gemm_pack_b.argtypes = [_I64, _I64, _P, _I64, _I32, _I32, _P, _I64, _P]
         L.gemm_quantize_fp8_rows.restype = _I32
         L.gemm_quantize_fp8_rows.argtypes = [_I64, _I64, _P, _I64, _P, _I64, _P, _P]
         L.gemm_workspace_size.restype = _SZ
@@ -237,6 +240,17 @@ def gemm_fp8_scaled_quant(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, sc
                                  workspace_bytes, _stream(stream))
     if st != 0:
         raise GemmError(st, "gemm_fp8_scaled_quant")
+
+
+def pack_b(K, N, B, ldb, layout_b, elem_bytes, Bp, ldbp, stream=None):
+    """One-time reorder of B (K x N) into K-major rows: Bp[n*ldbp + k] = b(k, n)."""
+    L = lib()
+    if K > 0 and N > 0:
+        _need(B, elem_bytes * (_extent(K, N, ldb) if layout_b == ROW else _extent(N, K, ldb)), "B")
+        _need(Bp, elem_bytes * _extent(N, K, ldbp), "Bp")
+    st = L.gemm_pack_b(K, N, _ptr(B), ldb, layout_b, elem_bytes, _ptr(Bp), ldbp, _stream(stream))
+    if st != 0:
+        raise GemmError(st, "gemm_pack_b")
 
 
 def quantize_fp8_rows(M, K, X, ldx, Q, ldq, scale, stream=None):

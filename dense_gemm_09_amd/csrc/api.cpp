@@ -332,6 +332,20 @@ gemm_status gemm_quantize_fp8_rows(int64_t M, int64_t K, const void* X, int64_t 
              ? GEMM_OK : GEMM_ERR_HIP;
 }
 
+gemm_status gemm_pack_b(int64_t K, int64_t N, const void* B, int64_t ldb, gemm_layout layout_b,
+                        int elem_bytes, void* Bp, int64_t ldbp, void* stream) {
+  if (!valid_layout(layout_b) || (elem_bytes != 1 && elem_bytes != 2)) return GEMM_ERR_BAD_ENUM;
+  if (K < 0 || N < 0 || K > kMaxDim || N > kMaxDim) return GEMM_ERR_BAD_DIM;
+  const bool rowmajor = layout_b == GEMM_ROW_MAJOR;
+  if (ldb < std::max<int64_t>(1, rowmajor ? N : K) || ldbp < std::max<int64_t>(1, K))
+    return GEMM_ERR_BAD_LD;
+  if (K == 0 || N == 0) return GEMM_OK;
+  if (B == nullptr || Bp == nullptr) return GEMM_ERR_NULL_POINTER;
+  if (rowmajor && ((K + 63) / 64) * ((N + 63) / 64) > INT32_MAX) return GEMM_ERR_BAD_DIM;
+  return launch_pack_b(K, N, B, ldb, rowmajor, elem_bytes, Bp, ldbp,
+                       static_cast<hipStream_t>(stream)) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
 size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int is_fp8) {
   if (M <= 0 || N <= 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   return make_plan(M, N, K, is_fp8 != 0).workspace;

@@ -51,4 +51,9 @@ hipError_t launch_splitk_reduce(const Plan& plan, const LaunchSpec& spec, const 
 hipError_t launch_quantize_rows(int64_t M, int64_t K, const void* X, int64_t ldx, void* Q,
                                 int64_t ldq, float* scale, bool vec, hipStream_t stream);
 
+// One-time reorder of B (K x N, elements of elem_bytes) into K-major rows of
+// ldbp elements (pack.hip). b_rowmajor: B is N-contiguous (b(k,n) = B[k*ldb+n]).
+hipError_t launch_pack_b(int64_t K, int64_t N, const void* B, int64_t ldb, bool b_rowmajor,
+                         int elem_bytes, void* Bp, int64_t ldbp, hipStream_t stream);
+
 }  // namespace g355

@@ -211,6 +211,28 @@ gemm_status gemm_quantize_fp8_rows(int64_t M, int64_t K, const void* X, int64_t 
                                    void* Q, int64_t ldq, float* scale, void* stream);
 
 /*
+ * One-time reorder of a weight matrix B (logical K x N) into the layout the
+ * fast path reads: Bp[n*ldbp + k] = b(k, n), i.e. GEMM_COL_MAJOR (K-major)
+ * with leading dimension ldbp. The FP8 DeepGEMM page (sec. 3.2) rearranges B
+ * once, before the calls that reuse it, so the reorder is paid once per
+ * weight. Pass the result to gemm_bf16 / gemm_fp8_scaled / gemm_mxfp8 with
+ * layout_b = GEMM_COL_MAJOR and ldb = ldbp; with ldbp * elem_bytes a multiple
+ * of 16, K * elem_bytes a multiple of 16 and Bp 16-byte aligned, B is then
+ * copied to on-chip memory by DMA (the fast path) instead of through
+ * registers.
+ * B: device, elements of elem_bytes (2: BF16, 1: E4M3; moved as bits), in
+ * layout_b (ROW: b(k,n) = B[k*ldb + n], ldb >= N; COL: B[n*ldb + k],
+ * ldb >= K). Bp: device, N rows of ldbp >= K elements; the elements k >= K of
+ * each row are not written. Bp must not overlap B.
+ * Errors (before anything is enqueued): GEMM_ERR_BAD_ENUM (layout_b,
+ * elem_bytes), GEMM_ERR_BAD_DIM (K or N negative or above 2^30),
+ * GEMM_ERR_BAD_LD, GEMM_ERR_NULL_POINTER (B or Bp when K, N > 0),
+ * GEMM_ERR_HIP. K == 0 or N == 0 does nothing.
+ */
+gemm_status gemm_pack_b(int64_t K, int64_t N, const void* B, int64_t ldb, gemm_layout layout_b,
+                        int elem_bytes, void* Bp, int64_t ldbp, void* stream);
+
+/*
  * Bytes of device workspace a call with these sizes needs (0 when the chosen
  * kernel needs none). Pure host arithmetic; callable without a GPU. Query
  * once and allocate up front (the FP8 page's interface, sec. 5.1, separates

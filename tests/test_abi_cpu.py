@@ -245,3 +245,22 @@ def test_mx_validation_before_launch():
     assert ws > 0
     assert mx(N=4096, K=2048, ldsa=64, ldsb=64) == NULLP
     assert mx(N=4096, K=2048, ldsa=64, ldsb=64, ws=FAKE, wsb=ws - 1) == WS_SMALL
+
+
+def pack(K=64, N=48, B=FAKE, ldb=None, lb=ROW, es=2, Bp=FAKE, ldbp=None):
+    ldb = (N if lb == ROW else K) if ldb is None else ldb
+    ldbp = K if ldbp is None else ldbp
+    return g.lib().gemm_pack_b(K, N, B, ldb, lb, es, Bp, ldbp, None)
+
+
+def test_pack_validation_before_launch():
+    assert pack(lb=2) == BAD_ENUM
+    assert pack(es=4) == BAD_ENUM
+    assert pack(K=-1) == BAD_DIM
+    assert pack(N=1 << 31) == BAD_DIM
+    assert pack(ldb=47) == BAD_LD            # ROW: ldb >= N
+    assert pack(lb=COL, ldb=63) == BAD_LD    # COL: ldb >= K
+    assert pack(ldbp=63) == BAD_LD
+    assert pack(B=None) == NULLP
+    assert pack(Bp=None) == NULLP
+    assert pack(K=0, B=None, Bp=None, ldbp=1) == OK
