@@ -108,6 +108,31 @@ def time_calls(fns, steps, warmup):
     return per, total, wall
 
 
+def time_blocks(fns, steps, warmup):
+    """`steps` steps of the callables, run callable by callable: all `steps`
+    calls of the first back to back, then of the second, ... (the same work as
+    `steps` interleaved steps). HIP events only at block edges on the current
+    stream, so a per-callable mean (ms) is its kernels' back-to-back time, with
+    no timing packet between launches. Returns (per-callable ms, total ms, wall s)."""
+    import torch
+    s = torch.cuda.current_stream()
+    for f in fns:
+        for _ in range(warmup):
+            f()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(s)
+    for j, f in enumerate(fns):
+        for _ in range(steps):
+            f()
+        ev[j + 1].record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[j].elapsed_time(ev[j + 1]) / steps for j in range(len(fns))]
+    return per, ev[0].elapsed_time(ev[-1]), wall
+
+
 def time_graph(fn, calls, reps=5):
     """Mean time per call (ms) of `calls` back-to-back calls captured in one HIP
     graph and replayed `reps` times (launch cost of the host side excluded, as in
@@ -222,7 +247,7 @@ def main():
 
     log(f"[bench] timing {args.steps} steps after {args.warmup} warmup")
     torch.cuda.synchronize()
-    per, total_ms, wall = time_calls([w_bf16, w_fp8], args.steps, args.warmup)
+    per, total_ms, wall = time_blocks([w_bf16, w_fp8], args.steps, args.warmup)
     torch.cuda.synchronize()
     ms_step = total_ms / args.steps
     fl_bf16, fl_fp8 = p_bf16.flops, p_fp8.flops
