@@ -349,7 +349,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
   // latency overlaps the epilogue math and stores of strip i. Quantised
   // outputs have no C_in.
   constexpr bool HAS_CIN = !SPLIT && (OUT == OUT_F32 || OUT == OUT_BF16);
-  float4 cin[2][E::ITERS];
+  // Double-buffered C_in, except where the FP32 C_in of a 256-wide FP8 tile
+  // would not fit next to its accumulators (it is then loaded per strip).
+  constexpr int CIN_BUFS = (C::FP8 && OUT == OUT_F32 && C::FN * C::FM >= 8) ? 1 : 2;
+  float4 cin[CIN_BUFS][E::ITERS];
   auto load_cin = [&](int i, float4 (&dst)[E::ITERS]) {
 #pragma unroll
     for (int it = 0; it < E::ITERS; ++it) {
@@ -375,7 +378,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
     }
   };
   const bool use_c = HAS_CIN && p.beta != 0.f;
-  if constexpr (HAS_CIN) {
+  if constexpr (HAS_CIN && CIN_BUFS == 2) {
     if (use_c) load_cin(0, cin[0]);
   }
 
@@ -411,7 +414,11 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
 #pragma unroll
   for (int i = 0; i < C::FM; ++i) {
     if constexpr (HAS_CIN) {
-      if (use_c && i + 1 < C::FM) load_cin(i + 1, cin[(i + 1) & 1]);
+      if constexpr (CIN_BUFS == 2) {
+        if (use_c && i + 1 < C::FM) load_cin(i + 1, cin[(i + 1) & 1]);
+      } else {
+        if (use_c) load_cin(i, cin[0]);
+      }
     }
     // accumulators of rows 32i..32i+31 -> LDS strip
 #pragma unroll
@@ -454,7 +461,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
           for (int q = 0; q < 4; ++q) v[q] = fmaf(v[q], cs[q], bias_v[q]);
         }
         if constexpr (HAS_CIN) {
-          const float4 cc = cin[i & 1][it];
+          const float4 cc = cin[CIN_BUFS == 2 ? (i & 1) : 0][it];
           const float c4[4] = {cc.x, cc.y, cc.z, cc.w};
 #pragma unroll
           for (int q = 0; q < 4; ++q)
