@@ -201,7 +201,7 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   if (K == 0) spec.loader_a = spec.loader_b = LOAD_DIRECT;  // nothing is loaded
 
   const bool direct = spec.loader_a == LOAD_DIRECT && spec.loader_b == LOAD_DIRECT;
-  // MX runs on the DMA-fed 256x128 / 128x128 tiles only (no skinny kernel).
+  // MX runs on the DMA-fed tile kernel only (no skinny kernel).
   if (mx && !direct) return GEMM_ERR_UNSUPPORTED;
   Plan p = (plan.kernel == KERNEL_SKINNY && (!direct || mx)) ? make_tile_plan(M, N, K, fp8) : plan;
   if (p.kernel == KERNEL_TILE && !direct) {
@@ -209,7 +209,6 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
     p.bn = 128;
     p.waves = 4;
   }
-  if (mx && p.bm == 256 && p.bn == 256) p.bn = 128;
   GemmArgs a{};
   a.A = A;
   a.B = B;

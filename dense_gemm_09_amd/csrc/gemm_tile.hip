@@ -882,8 +882,9 @@ using Mid8 = TileCfg<256, 128, 4, 2, true, 128, 2, 2>;
 using Small16 = TileCfg<128, 128, 2, 2, false, 128, 2>;
 using Small8 = TileCfg<128, 128, 2, 2, true, 128, 2>;
 // MX (E8M0 block-scaled) FP8: the scale words take up to 12 more VGPRs per
-// lane, which the 256x256 FP8 tile (at the 256-register limit) does not have;
-// its plans run on 256x128.
+// lane. With the slice's loads spread over both k-steps the 256x256 loop has
+// room for them.
+using Big8X = TileCfg<256, 256, 2, 4, true, 128, 2, 2, true>;
 using Mid8X = TileCfg<256, 128, 4, 2, true, 128, 2, 2, true>;
 using Small8X = TileCfg<128, 128, 2, 2, true, 128, 2, 1, true>;
 
@@ -896,6 +897,8 @@ hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs&
   if (spec.mx) {
     // MX operands take the DMA loader only (checked by the caller).
     if (!direct) return hipErrorInvalidValue;
+    if (plan.bm == 256 && plan.bn == 256)
+      return launch_cfg<Big8X, LOAD_DIRECT, LOAD_DIRECT, false>(plan, spec, a, stream);
     if (plan.bm == 256)
       return launch_cfg<Mid8X, LOAD_DIRECT, LOAD_DIRECT, false>(plan, spec, a, stream);
     return launch_cfg<Small8X, LOAD_DIRECT, LOAD_DIRECT, false>(plan, spec, a, stream);
