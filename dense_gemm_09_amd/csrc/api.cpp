@@ -198,12 +198,20 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
                       ? LOAD_DIRECT : LOAD_GENERIC;
   spec.loader_b = (spec.b_kmajor && k_ok && ldb % ce == 0 && aligned16(B) && under2g(N, ldb))
                       ? LOAD_DIRECT : LOAD_GENERIC;
+  // BF16 B stored N-contiguous: DMA into an N-major tile (transposing reads)
+  // when its rows are 16-byte aligned, N is a multiple of 8 and A is DMA-fed.
+  if (!fp8 && !spec.b_kmajor && spec.loader_a == LOAD_DIRECT && ldb % 8 == 0 && N % 8 == 0 &&
+      aligned16(B) && ((K - 1) * ldb + N) * es < (int64_t{1} << 31))
+    spec.loader_b = LOAD_DIRECT_N;
   if (K == 0) spec.loader_a = spec.loader_b = LOAD_DIRECT;  // nothing is loaded
 
-  const bool direct = spec.loader_a == LOAD_DIRECT && spec.loader_b == LOAD_DIRECT;
+  const bool direct = spec.loader_a == LOAD_DIRECT &&
+                      (spec.loader_b == LOAD_DIRECT || spec.loader_b == LOAD_DIRECT_N);
   // MX runs on the DMA-fed tile kernel only (no skinny kernel).
   if (mx && !direct) return GEMM_ERR_UNSUPPORTED;
-  Plan p = (plan.kernel == KERNEL_SKINNY && (!direct || mx)) ? make_tile_plan(M, N, K, fp8) : plan;
+  // The skinny kernel reads K-major operands only.
+  const bool skinny_ok = direct && !mx && spec.loader_b == LOAD_DIRECT;
+  Plan p = (plan.kernel == KERNEL_SKINNY && !skinny_ok) ? make_tile_plan(M, N, K, fp8) : plan;
   if (p.kernel == KERNEL_TILE && !direct) {
     p.bm = 128;
     p.bn = 128;

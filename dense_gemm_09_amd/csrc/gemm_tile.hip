@@ -166,6 +166,63 @@ struct DirectLoader {
   }
 };
 
+// ------------------------------------------------ DMA loader, N-contiguous B
+
+// B stored N-contiguous (BF16, row-major K x N): a slice's BKE rows of k are
+// copied as they lie in memory into an N-major LDS tile (one row of BN*2
+// bytes per k), 16-byte chunk c of row k at physical chunk c ^ (4 * (k % 4)):
+// a transposing fragment read (ds_read_b64_tr_b16) takes four consecutive k
+// rows at once, and the XOR puts those rows on different banks. As with the
+// K-major loader the swizzle is applied by the source address each DMA lane
+// fetches. Every byte offset is in the per-lane offset (row * ldb * 2 +
+// column * 2, the slice's k0 * ldb * 2 added per slice), so the buffer range
+// check turns rows past the last k and chunks past the array into zeros;
+// chunks at or past N (N is a multiple of 8) get the out-of-range offset.
+template <class C, int NW = C::NWAVES>
+struct NmajorLoader {
+  static constexpr int ROWN = C::BN * 2;     // bytes per LDS row (one k)
+  static constexpr int CPRN = ROWN / 16;     // 16-byte chunks per row
+  static constexpr int RPSN = 1024 / ROWN;   // rows per 1 KB DMA segment
+  static constexpr int SEGS = C::BKE / RPSN; // segments per slice
+  static constexpr int IPW = SEGS / NW;
+  static_assert(1024 % ROWN == 0 && SEGS % NW == 0, "N-major B tile");  // used for BF16 only
+  uint32_t off[IPW];  // row * ldb * 2 + column bytes of this lane's chunk, or `oob`
+  uint32_t ldb2;      // bytes per row of B
+  int lrow;           // this lane's row inside a segment
+
+  __device__ __forceinline__ void init(int64_t ldb, int n0, int N, uint32_t oob, int wave,
+                                       int lane) {
+    ldb2 = static_cast<uint32_t>(ldb * 2);
+    lrow = lane / CPRN;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r = (wave * IPW + i) * RPSN + lrow;
+      const int lc = (lane % CPRN) ^ (4 * (r & 3));
+      const int n = n0 + 8 * lc;
+      off[i] = n < N ? static_cast<uint32_t>(static_cast<int64_t>(r) * ldb * 2 + n * 2) : oob;
+    }
+  }
+
+  // Same interface as DirectLoader::issue_buf (koff unused: the slice offset
+  // k0 * ldb * 2 goes into the per-lane offset so the range check covers it).
+  template <int I0 = 0, int I1 = IPW>
+  __device__ __forceinline__ void issue_buf(char* lds_tile, int wave, __amdgpu_buffer_rsrc_t rsrc,
+                                            int koff, uint32_t oob, int k0, int k_end,
+                                            bool full) const {
+    (void)koff;
+    const uint32_t kbytes = static_cast<uint32_t>(k0) * ldb2;
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+      const int s = wave * IPW + i;
+      const int r = s * RPSN + lrow;
+      // off[i] == oob stays past the extent after the add (both are below 2^31).
+      const uint32_t vo = (full || k0 + r < k_end) ? off[i] + kbytes : oob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (G355_LDS void*)(lds_tile + s * 1024), 16,
+                                               static_cast<int>(vo), 0, 0, 0);
+    }
+  }
+};
+
 // ------------------------------------------------------------- register loader
 
 template <class C, int ROWS>
@@ -222,6 +279,8 @@ struct GenericLoader {
 };
 
 // ------------------------------------------------------------ MFMA schedule
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <bool FP8> struct FragOf { using type = bf16x8; };   // 8 BF16: one ds_read_b128
 template <> struct FragOf<true> { using type = i32x8; };     // 32 FP8: two ds_read_b128
@@ -531,6 +590,8 @@ gemm_tile_kernel(GemmArgs p) {
   // ---- loaders
   DirectLoader<C, C::BM> da;
   DirectLoader<C, C::BN> db;
+  using NLoader = NmajorLoader<C>;
+  NLoader dn;
   GenericLoader<C, C::BM> ga;
   GenericLoader<C, C::BN> gb;
   if constexpr (LA == LOAD_DIRECT) {
@@ -539,14 +600,30 @@ gemm_tile_kernel(GemmArgs p) {
     ga.base = static_cast<const char*>(p.A); ga.ld = p.lda; ga.row0 = m0; ga.rows = p.M;
     ga.kmajor = p.a_mn_major == 0;
   }
+  // Buffer descriptors over each operand's extent (under 2 GiB, checked on
+  // the host, so an offset past the extent plus the slice offset cannot wrap
+  // into range).
+  const uint32_t ext_a = static_cast<uint32_t>(
+      (static_cast<int64_t>(p.M - 1) * p.lda + p.K) * C::ES);
+  const uint32_t ext_b = static_cast<uint32_t>(
+      LB == LOAD_DIRECT_N ? (static_cast<int64_t>(p.K - 1) * p.ldb + p.N) * C::ES
+                          : (static_cast<int64_t>(p.N - 1) * p.ldb + p.K) * C::ES);
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.A), 0, static_cast<int>(ext_a), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(p.B), 0, static_cast<int>(ext_b), kBufferWord3);
   if constexpr (LB == LOAD_DIRECT) {
     db.init(p.ldb, n0, p.N, wave, lane);
+  } else if constexpr (LB == LOAD_DIRECT_N) {
+    dn.init(p.ldb, n0, p.N, ext_b, wave, lane);
   } else {
     gb.base = static_cast<const char*>(p.B); gb.ld = p.ldb; gb.row0 = n0; gb.rows = p.N;
     gb.kmajor = p.b_mn_major == 0;
   }
   constexpr int DMA_PER_SLICE = (LA == LOAD_DIRECT ? DirectLoader<C, C::BM>::IPW : 0) +
-                                (LB == LOAD_DIRECT ? DirectLoader<C, C::BN>::IPW : 0);
+                                (LB == LOAD_DIRECT     ? DirectLoader<C, C::BN>::IPW
+                                 : LB == LOAD_DIRECT_N ? NLoader::IPW
+                                                       : 0);
   // At boundary j the loads of slice j+1 must be complete; those of slices
   // j+2 .. j+STAGES-1 (issued at the STAGES-2 boundaries before) may still
   // be in flight. Register-loaded slices are already in LDS by then.
@@ -564,11 +641,13 @@ gemm_tile_kernel(GemmArgs p) {
     if constexpr (LB == LOAD_DIRECT)
       db.issue(b_tile(st), wave, static_cast<const char*>(p.B) + static_cast<int64_t>(k0) * C::ES,
                k0, k_end, full);
+    else if constexpr (LB == LOAD_DIRECT_N)
+      dn.issue_buf(b_tile(st), wave, rsrc_b, 0, ext_b, k0, k_end, full);
     else gb.load(tid, k0, k_end);
   };
   auto commit = [&](int st) __attribute__((always_inline)) {
-    if constexpr (LA != LOAD_DIRECT) ga.store(a_tile(st), tid);
-    if constexpr (LB != LOAD_DIRECT) gb.store(b_tile(st), tid);
+    if constexpr (LA == LOAD_GENERIC) ga.store(a_tile(st), tid);
+    if constexpr (LB == LOAD_GENERIC) gb.store(b_tile(st), tid);
   };
 
   // ---- per-lane fragment addresses (bytes inside a tile)
@@ -578,6 +657,19 @@ gemm_tile_kernel(GemmArgs p) {
   const int half = lane >> 5;
   const int a_row = (wm0 + (lane & 31)) * C::ROWB;
   const int b_row = (wn0 + (lane & 31)) * C::ROWB;
+  // N-major B: within each group of 16 lanes, lane j points its transposing
+  // read at row (j / 4) of a 4-row band and columns 4*(j % 4) .. +3 of the
+  // group's 16 columns; lane i then receives column i of the 4 rows. kq =
+  // (lane%16)/4 is the lane's row in the band, so its chunks are XORed with 4*kq.
+  int ntr_row = 0, ntr_col[C::FN];
+  if constexpr (LB == LOAD_DIRECT_N) {
+    const int kq = (lane & 15) >> 2;
+    ntr_row = (8 * half + kq) * NLoader::ROWN + 8 * (lane & 1);
+    const int lc0 = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      ntr_col[j] = ((((wn0 + 32 * j) >> 3) ^ (4 * kq)) + lc0) << 4;
+  }
 
   f32x16 acc[C::FM][C::FN];
 #pragma unroll
@@ -601,9 +693,22 @@ gemm_tile_kernel(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
         fa[i] = *reinterpret_cast<const bf16x8*>(at + a_row + i * 32 * C::ROWB + co);
+      if constexpr (LB == LOAD_DIRECT_N) {
+        // k rows 16t + 8*half + 0..7 of the lane's column, as two transposing
+        // reads of four rows each (rows 16t + 8*half + 4r + kq, kq = (lane%16)/4).
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(bt + b_row + j * 32 * C::ROWB + co);
+        for (int j = 0; j < C::FN; ++j) {
+          const char* q = bt + ntr_row + ntr_col[j] + (16 * t) * NLoader::ROWN;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((G355_LDS s16x4*)(q));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (G355_LDS s16x4*)(q + 4 * NLoader::ROWN));
+          fb[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          fb[j] = *reinterpret_cast<const bf16x8*>(bt + b_row + j * 32 * C::ROWB + co);
+      }
     } else {
       // Registers 0-3 and 4-7 of a lane take two 16-byte chunks of its row.
       // The MX scaled MFMA treats registers 0-3 of lanes i and i+32 as one
@@ -675,35 +780,34 @@ gemm_tile_kernel(GemmArgs p) {
   // of the next slice, and a slice's loads have STAGES-1 slices of MFMA work
   // to arrive. Register-loaded operands hold the slice fetched at boundary j
   // in registers and write it to LDS just before boundary j+1.
-  constexpr int READS = C::FP8 ? 2 * (C::FM + C::FN) : C::FM + C::FN;
+  // LDS fragment reads per k-step (an N-major B block takes two 8-byte
+  // transposing reads).
+  constexpr int READS = C::FP8              ? 2 * (C::FM + C::FN)
+                        : LB == LOAD_DIRECT_N ? C::FM + 2 * C::FN
+                                              : C::FM + C::FN;
   constexpr int MFMAS = C::FM * C::FN;
-  constexpr bool ALL_DMA = LA == LOAD_DIRECT && LB == LOAD_DIRECT;
+  constexpr bool ALL_DMA = LA == LOAD_DIRECT && (LB == LOAD_DIRECT || LB == LOAD_DIRECT_N);
   // With both operands on the DMA path, the loads of slice s are issued in
   // SPREAD parts: part 0 at boundary s-STAGES, part p in the (p-1)-th k-step
   // after it, so that the loads of all waves do not queue up at once.
   constexpr int NA = LA == LOAD_DIRECT ? DirectLoader<C, C::BM>::IPW : 0;
-  constexpr int NB = LB == LOAD_DIRECT ? DirectLoader<C, C::BN>::IPW : 0;
+  constexpr int NB = LB == LOAD_DIRECT     ? DirectLoader<C, C::BN>::IPW
+                     : LB == LOAD_DIRECT_N ? NLoader::IPW
+                                           : 0;
   using Part0 = DmaPart<C, NA, NB, 0>;
   using Part1 = DmaPart<C, NA, NB, 1>;
   using Part2 = DmaPart<C, NA, NB, 2>;
   using Part3 = DmaPart<C, NA, NB, 3>;
-  // Buffer descriptors over each operand's extent (under 2 GiB, checked on
-  // the host, so an offset past the extent plus the slice offset cannot wrap
-  // into range).
-  const uint32_t ext_a = static_cast<uint32_t>(
-      (static_cast<int64_t>(p.M - 1) * p.lda + p.K) * C::ES);
-  const uint32_t ext_b = static_cast<uint32_t>(
-      (static_cast<int64_t>(p.N - 1) * p.ldb + p.K) * C::ES);
-  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(p.A), 0, static_cast<int>(ext_a), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rsrc_b = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(p.B), 0, static_cast<int>(ext_b), kBufferWord3);
   auto dma_part = [&](auto part, int s) {
     using Pt = decltype(part);
     const int k0 = k_begin + s * C::BKE;
     const int st = s % C::STAGES;
-    Pt::issue(da, db, a_tile(st), b_tile(st), wave, rsrc_a, rsrc_b, ext_a, ext_b, k0 * C::ES, k0,
-              k_end, k0 + C::BKE <= k_end);
+    if constexpr (LB == LOAD_DIRECT_N)
+      Pt::issue(da, dn, a_tile(st), b_tile(st), wave, rsrc_a, rsrc_b, ext_a, ext_b, k0 * C::ES,
+                k0, k_end, k0 + C::BKE <= k_end);
+    else
+      Pt::issue(da, db, a_tile(st), b_tile(st), wave, rsrc_a, rsrc_b, ext_a, ext_b, k0 * C::ES,
+                k0, k_end, k0 + C::BKE <= k_end);
   };
   // ---- MX scale words. Every byte offset (row * ld + 4 * slice) is in the
   // per-lane offset and checked against the array's extent by the buffer
@@ -894,6 +998,15 @@ hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs&
   a.a_mn_major = spec.a_kmajor ? 0 : 1;
   a.b_mn_major = spec.b_kmajor ? 0 : 1;
   const bool direct = spec.loader_a == LOAD_DIRECT && spec.loader_b == LOAD_DIRECT;
+  if (spec.loader_b == LOAD_DIRECT_N) {
+    // BF16, K-major A by DMA, N-contiguous B by DMA (checked by the caller).
+    if (spec.fp8 || spec.loader_a != LOAD_DIRECT) return hipErrorInvalidValue;
+    if (plan.bm == 256 && plan.bn == 256)
+      return launch_cfg<Big16, LOAD_DIRECT, LOAD_DIRECT_N>(plan, spec, a, stream);
+    if (plan.bm == 256 && plan.bn == 128)
+      return launch_cfg<Mid16, LOAD_DIRECT, LOAD_DIRECT_N>(plan, spec, a, stream);
+    return launch_cfg<Small16, LOAD_DIRECT, LOAD_DIRECT_N>(plan, spec, a, stream);
+  }
   if (spec.mx) {
     // MX operands take the DMA loader only (checked by the caller).
     if (!direct) return hipErrorInvalidValue;

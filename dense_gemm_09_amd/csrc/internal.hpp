@@ -13,6 +13,8 @@ namespace g355 {
 enum Loader : int {
   LOAD_DIRECT = 0,   // K-major, 16-byte aligned rows: global -> LDS DMA, no registers
   LOAD_GENERIC = 1,  // any layout / alignment: element loads through registers
+  LOAD_DIRECT_N = 2, // B only, BF16 N-contiguous (row-major), 16-byte aligned rows, N % 8 == 0:
+                     // DMA into an N-major LDS tile, fragments by transposing LDS reads
 };
 
 enum KernelKind : int { KERNEL_TILE = 0, KERNEL_SKINNY = 1 };
