@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm355.so")
-SOURCES = ["api.cpp", "gemm_tile.hip", "gemm_skinny.hip", "quant.hip", "pack.hip"]
+SOURCES = ["api.cpp", "gemm_tile.hip", "gemm_tile_ragged.hip", "gemm_skinny.hip", "quant.hip",
+           "pack.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

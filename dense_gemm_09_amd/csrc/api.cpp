@@ -189,15 +189,21 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   const bool k_ok = K % ce == 0;
   // The DMA loader addresses an operand with 32-bit byte offsets from its base
   // and marks chunks past K with an offset just beyond the operand's extent:
-  // the extent must stay under 2 GiB.
+  // the extent must stay under 2 GiB. K need not be a multiple of the 16-byte
+  // chunk (the kernel writes each row's last, partial chunk itself). Rows are
+  // 16-byte aligned, or, for BF16, at any 2-byte alignment (buffer loads take
+  // unaligned addresses; byte-aligned E4M3 rows go through the register loader).
   const int64_t es = fp8 ? 1 : 2;
   const auto under2g = [&](int64_t rows, int64_t ld) {
     return ((rows - 1) * ld + K) * es < (int64_t{1} << 31);
   };
-  spec.loader_a = (spec.a_kmajor && k_ok && lda % ce == 0 && aligned16(A) && under2g(M, lda))
-                      ? LOAD_DIRECT : LOAD_GENERIC;
-  spec.loader_b = (spec.b_kmajor && k_ok && ldb % ce == 0 && aligned16(B) && under2g(N, ldb))
-                      ? LOAD_DIRECT : LOAD_GENERIC;
+  const auto rows16 = [&](const void* p, int64_t ld) { return aligned16(p) && ld % ce == 0; };
+  const auto dma_ok = [&](bool kmajor, const void* p, int64_t ld, int64_t rows) {
+    const bool even = (reinterpret_cast<uintptr_t>(p) & 1u) == 0;
+    return kmajor && under2g(rows, ld) && (rows16(p, ld) || (!fp8 && even));
+  };
+  spec.loader_a = dma_ok(spec.a_kmajor, A, lda, M) ? LOAD_DIRECT : LOAD_GENERIC;
+  spec.loader_b = dma_ok(spec.b_kmajor, B, ldb, N) ? LOAD_DIRECT : LOAD_GENERIC;
   // BF16 B stored N-contiguous: DMA into an N-major tile (transposing reads)
   // when its rows are 16-byte aligned, N is a multiple of 8 and A is DMA-fed.
   if (!fp8 && !spec.b_kmajor && spec.loader_a == LOAD_DIRECT && ldb % 8 == 0 && N % 8 == 0 &&
@@ -209,8 +215,15 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
                       (spec.loader_b == LOAD_DIRECT || spec.loader_b == LOAD_DIRECT_N);
   // MX runs on the DMA-fed tile kernel only (no skinny kernel).
   if (mx && !direct) return GEMM_ERR_UNSUPPORTED;
-  // The skinny kernel reads K-major operands only.
-  const bool skinny_ok = direct && !mx && spec.loader_b == LOAD_DIRECT;
+  // K ends inside a 16-byte chunk of a DMA-fed K-major row: the tile kernels
+  // that write that chunk themselves. (FP8 with one operand not DMA-fed reads
+  // both through registers.)
+  spec.ragged = !k_ok && (direct || (!fp8 && (spec.loader_a == LOAD_DIRECT ||
+                                              spec.loader_b == LOAD_DIRECT)));
+  // The skinny kernel reads K-major operands with 16-byte aligned rows and K a
+  // multiple of the chunk only.
+  const bool skinny_ok = direct && !mx && spec.loader_b == LOAD_DIRECT && k_ok &&
+                         rows16(A, lda) && rows16(B, ldb);
   Plan p = (plan.kernel == KERNEL_SKINNY && !skinny_ok) ? make_tile_plan(M, N, K, fp8) : plan;
   if (p.kernel == KERNEL_TILE && !direct) {
     p.bm = 128;

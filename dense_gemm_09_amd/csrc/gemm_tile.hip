@@ -44,10 +44,6 @@ namespace g355 {
 // no swizzle, no index stride).
 constexpr int kBufferWord3 = 0x00020000;
 
-// A 16-byte block of zeros in global memory, read by loads whose chunk lies
-// at or past the end of K.
-__device__ __attribute__((aligned(16))) uint32_t g_zero16[4] = {0u, 0u, 0u, 0u};
-
 // Physical chunk offset of row r for CPR chunks per row (see file comment).
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
@@ -97,14 +93,17 @@ struct DirectLoader {
   // NW waves issue the loads of a tile; each issues IPW 1 KB segments per slice.
   static constexpr int IPW = ROWS / C::RPS / NW;
   // Byte offset of this lane's chunk (row start + chunk, k excluded) from the
-  // operand base. Offsets are 32-bit (operands under 4 GiB, checked on the
-  // host), so a load is the wave-uniform base (SGPRs) plus one VGPR: the
-  // per-slice advance is a scalar add.
+  // operand base. Offsets are 32-bit (operands under 2 GiB, checked on the
+  // host), so a load is one VGPR plus the slice's wave-uniform offset (an
+  // SGPR): the per-slice advance is a scalar add. Rows need not be 16-byte
+  // aligned (BF16 rows at any 2-byte alignment: buffer loads take unaligned
+  // addresses).
   uint32_t off[IPW];
-  // First K element of the lane's chunk in segments of even and of odd index:
-  // a segment holds RPS consecutive rows starting at a multiple of RPS, so the
-  // swizzle of a lane's row depends on the segment only through its parity.
-  int kc2[2];
+  // One past the last K element of the lane's chunk (slice-relative) in
+  // segments of even and of odd index: a segment holds RPS consecutive rows
+  // starting at a multiple of RPS, so the swizzle of a lane's row depends on
+  // the segment only through its parity.
+  int kce2[2];
 
   __device__ __forceinline__ void init(int64_t ld, int row0, int rows, int wave, int lane) {
 #pragma unroll
@@ -119,15 +118,19 @@ struct DirectLoader {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int r = C::RPS * q + lane / C::CPR;
-      kc2[q] = ((lane % C::CPR) ^ swz<C::CPR>(r)) * C::CE;
+      kce2[q] = ((lane % C::CPR) ^ swz<C::CPR>(r)) * C::CE + C::CE;
     }
   }
 
   // Loads of a slice as buffer loads: the operand's descriptor (whose range
   // is the operand's extent), this lane's 32-bit offset and the slice's
-  // wave-uniform byte offset koff = k0 * ES. Lanes whose chunk starts at or
-  // past k_end use the offset `oob` (the extent): the buffer's range check
-  // turns their load into zeros. full: no lane of the slice is past k_end.
+  // wave-uniform byte offset koff = k0 * ES. Only chunks that end at or before
+  // k_end are copied; the others use the offset `oob` (the extent), which the
+  // buffer's range check turns into zeros without a memory access. (The range
+  // check sees the per-lane offset only, not koff, so a chunk that straddles
+  // k_end is never copied: on the operand's last row its bytes past K may lie
+  // past the allocation. Such chunks are written by patch_tail.)
+  // full: every chunk of the slice ends at or before k_end.
   template <int I0 = 0, int I1 = IPW>
   __device__ __forceinline__ void issue_buf(char* lds_tile, int wave, __amdgpu_buffer_rsrc_t rsrc,
                                             int koff, uint32_t oob, int k0, int k_end,
@@ -135,33 +138,9 @@ struct DirectLoader {
 #pragma unroll
     for (int i = I0; i < I1; ++i) {
       const int s = wave * IPW + i;
-      const uint32_t vo = (full || k0 + kc2[s & 1] < k_end) ? off[i] : oob;
+      const uint32_t vo = (full || k0 + kce2[s & 1] <= k_end) ? off[i] : oob;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (G355_LDS void*)(lds_tile + s * 1024), 16,
                                                static_cast<int>(vo), koff, 0, 0);
-    }
-  }
-
-  // base: operand pointer advanced to element k0 (wave-uniform). full: the
-  // whole slice lies below k_end (wave-uniform), so no lane needs a bound check.
-  template <int I0 = 0, int I1 = IPW>
-  __device__ __forceinline__ void issue(char* lds_tile, int wave, const char* base, int k0,
-                                        int k_end, bool full) const {
-    if (full) {
-#pragma unroll
-      for (int i = I0; i < I1; ++i) {
-        const int s = wave * IPW + i;
-        __builtin_amdgcn_global_load_lds((const G355_GLOBAL void*)(base + off[i]),
-                                         (G355_LDS void*)(lds_tile + s * 1024), 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int i = I0; i < I1; ++i) {
-        const int s = wave * IPW + i;
-        const char* g = (k0 + kc2[s & 1] < k_end) ? base + off[i]
-                                             : reinterpret_cast<const char*>(g_zero16);
-        __builtin_amdgcn_global_load_lds((const G355_GLOBAL void*)(g),
-                                         (G355_LDS void*)(lds_tile + s * 1024), 16, 0, 0);
-      }
     }
   }
 };
@@ -562,7 +541,10 @@ __device__ __forceinline__ void run_epilogue(const GemmArgs& p, const f32x16 (&a
 
 // ------------------------------------------------------------------- the kernel
 
-template <class C, int LA, int LB, int OUT, bool SPLIT>
+// RAGGED: K may end inside a 16-byte chunk of a DMA-fed row (patch_tail).
+// Kept out of the other instantiations: the patch's code perturbs the
+// register allocation of the K loop.
+template <class C, int LA, int LB, int OUT, bool SPLIT, bool RAGGED>
 __global__ void __launch_bounds__(C::NT)
 gemm_tile_kernel(GemmArgs p) {
   // The LDS block holds the ring of K slices, and after the main loop the
@@ -635,12 +617,10 @@ gemm_tile_kernel(GemmArgs p) {
   auto fetch = [&](int st, int k0) __attribute__((always_inline)) {
     const bool full = k0 + C::BKE <= k_end;
     if constexpr (LA == LOAD_DIRECT)
-      da.issue(a_tile(st), wave, static_cast<const char*>(p.A) + static_cast<int64_t>(k0) * C::ES,
-               k0, k_end, full);
+      da.issue_buf(a_tile(st), wave, rsrc_a, k0 * C::ES, ext_a, k0, k_end, full);
     else ga.load(tid, k0, k_end);
     if constexpr (LB == LOAD_DIRECT)
-      db.issue(b_tile(st), wave, static_cast<const char*>(p.B) + static_cast<int64_t>(k0) * C::ES,
-               k0, k_end, full);
+      db.issue_buf(b_tile(st), wave, rsrc_b, k0 * C::ES, ext_b, k0, k_end, full);
     else if constexpr (LB == LOAD_DIRECT_N)
       dn.issue_buf(b_tile(st), wave, rsrc_b, 0, ext_b, k0, k_end, full);
     else gb.load(tid, k0, k_end);
@@ -648,6 +628,57 @@ gemm_tile_kernel(GemmArgs p) {
   auto commit = [&](int st) __attribute__((always_inline)) {
     if constexpr (LA == LOAD_GENERIC) ga.store(a_tile(st), tid);
     if constexpr (LB == LOAD_GENERIC) gb.store(b_tile(st), tid);
+  };
+  // K range ending inside a 16-byte chunk (K not a multiple of CE, last
+  // split): the DMA copies no chunk that straddles k_end, so in the last
+  // slice (stage st, once its copies have landed) each K-major DMA-fed row
+  // gets that chunk written here: its elements below k_end, then zeros. The
+  // tail tile then runs the full-tile MFMA path, as with zero-filled boundary
+  // loads. Ends with a barrier that publishes the chunks.
+  static_assert(!RAGGED || LA == LOAD_DIRECT || LB == LOAD_DIRECT, "ragged: a DMA-fed row");
+  const bool ragged = k_end % C::CE != 0;
+  auto patch_tail = [&](int st) {
+    constexpr int RA = LA == LOAD_DIRECT ? C::BM : 0;
+    constexpr int ROWS = RA + (LB == LOAD_DIRECT ? C::BN : 0);
+    const int kc = k_end - k_end % C::CE;   // first element of the straddling chunk
+    const int nb = (k_end - kc) * C::ES;    // its bytes below k_end: 1 .. 15
+    const int cl = (kc - (k_begin + (nk - 1) * C::BKE)) / C::CE;  // its chunk in the slice
+    // The thread index passes through an opaque move, so that none of the
+    // per-lane address arithmetic below is hoisted out of the K loop (where
+    // it would hold registers for the whole loop).
+    int t;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(tid));
+#pragma unroll
+    for (int q0 = 0; q0 < ROWS; q0 += C::NT) {
+      const int q = q0 + t;
+      if (ROWS % C::NT != 0 && q >= ROWS) break;
+      const bool is_a = q < RA;
+      const int r = is_a ? q : q - RA;
+      const int rows = is_a ? p.M : p.N;
+      int g = (is_a ? m0 : n0) + r;
+      g = g < rows ? g : rows - 1;  // rows past the operand repeat its last row, as the DMA does
+      const uintptr_t src = reinterpret_cast<uintptr_t>(is_a ? p.A : p.B) +
+                            (static_cast<int64_t>(g) * (is_a ? p.lda : p.ldb) + kc) * C::ES;
+      // The valid bytes, read as the 4-byte aligned words that hold them (each
+      // such word holds at least one byte of the operand, so no read leaves
+      // the operand's pages), then shifted into place; bytes past k_end are 0.
+      const uint32_t* wp = reinterpret_cast<const uint32_t*>(src & ~uintptr_t{3});
+      const int sh = static_cast<int>(src & 3);
+      const int ndw = (sh + nb + 3) >> 2;   // 1 .. 5
+      uint32_t d[5];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) d[i] = i < ndw ? wp[i] : 0u;
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t v = __builtin_amdgcn_alignbyte(d[i + 1], d[i], sh);
+        const int keep = nb - 4 * i;        // valid bytes of word i
+        w[i] = keep >= 4 ? v : keep <= 0 ? 0u : (v & ((1u << (8 * keep)) - 1u));
+      }
+      char* dst = (is_a ? a_tile(st) : b_tile(st)) + r * C::ROWB + ((cl ^ swz<C::CPR>(r)) << 4);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
 
   // ---- per-lane fragment addresses (bytes inside a tile)
@@ -853,6 +884,9 @@ gemm_tile_kernel(GemmArgs p) {
   auto boundary = [&](int j) {
     commit((j + C::STAGES - 1) % C::STAGES);
     wait_loads_and_barrier<DMA_BEHIND>();
+    if constexpr (RAGGED) {
+      if (ragged && j + 1 == nk - 1) patch_tail((j + 1) % C::STAGES);
+    }
     if constexpr (ALL_DMA) dma_part(Part0{}, j + C::STAGES);
     else fetch(j % C::STAGES, k_begin + (j + C::STAGES) * C::BKE);
   };
@@ -893,6 +927,9 @@ gemm_tile_kernel(GemmArgs p) {
     }
     if constexpr (C::MX) mx_load(0);
     wait_loads_and_barrier<DMA_BEHIND>();
+    if constexpr (RAGGED) {
+      if (ragged && nk == 1) patch_tail(0);
+    }
     if constexpr (C::MX) mx_ready(0);
     fetch(C::STAGES - 1, k_begin + (C::STAGES - 1) * C::BKE);
     reads(0, 0, fa0, fb0);
@@ -949,26 +986,30 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs p) {
 // ------------------------------------------------------------------- launchers
 #ifndef G355_KERNELS_ONLY
 
-template <class C, int LA, int LB, bool QUANT_OUT = true>
+template <class C, int LA, int LB, bool RAGGED, bool QUANT_OUT = true>
 static hipError_t launch_cfg(const Plan& plan, const LaunchSpec& spec, const GemmArgs& a,
                              hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(plan.grid)), block(C::NT);
   if (plan.split > 1) {
-    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_F32, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_F32, true, RAGGED>), grid, block, 0,
+                       stream, a);
   } else if (spec.out == OUT_BF16) {
-    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_BF16, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_BF16, false, RAGGED>), grid, block, 0,
+                       stream, a);
   } else if (spec.out == OUT_I8 || spec.out == OUT_E4M3) {
     if constexpr (QUANT_OUT) {
       if (spec.out == OUT_I8)
-        hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_I8, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_I8, false, RAGGED>), grid, block, 0,
+                           stream, a);
       else
-        hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_E4M3, false>), grid, block, 0, stream,
-                           a);
+        hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_E4M3, false, RAGGED>), grid, block, 0,
+                           stream, a);
     } else {
       return hipErrorInvalidValue;
     }
   } else {
-    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_F32, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_F32, false, RAGGED>), grid, block, 0,
+                       stream, a);
   }
   return hipGetLastError();
 }
@@ -992,8 +1033,11 @@ using Big8X = TileCfg<256, 256, 2, 4, true, 128, 2, 2, true>;
 using Mid8X = TileCfg<256, 128, 4, 2, true, 128, 2, 2, true>;
 using Small8X = TileCfg<128, 128, 2, 2, true, 128, 2, 1, true>;
 
-hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
-                       hipStream_t stream) {
+// The launches of launch_tile, with the kernels' RAGGED flag R. Register
+// loading of both operands has no ragged variant (it bounds every element).
+template <bool R>
+static hipError_t launch_tile_t(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
+                                hipStream_t stream) {
   GemmArgs a = args;
   a.a_mn_major = spec.a_kmajor ? 0 : 1;
   a.b_mn_major = spec.b_kmajor ? 0 : 1;
@@ -1002,37 +1046,53 @@ hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs&
     // BF16, K-major A by DMA, N-contiguous B by DMA (checked by the caller).
     if (spec.fp8 || spec.loader_a != LOAD_DIRECT) return hipErrorInvalidValue;
     if (plan.bm == 256 && plan.bn == 256)
-      return launch_cfg<Big16, LOAD_DIRECT, LOAD_DIRECT_N>(plan, spec, a, stream);
+      return launch_cfg<Big16, LOAD_DIRECT, LOAD_DIRECT_N, R>(plan, spec, a, stream);
     if (plan.bm == 256 && plan.bn == 128)
-      return launch_cfg<Mid16, LOAD_DIRECT, LOAD_DIRECT_N>(plan, spec, a, stream);
-    return launch_cfg<Small16, LOAD_DIRECT, LOAD_DIRECT_N>(plan, spec, a, stream);
+      return launch_cfg<Mid16, LOAD_DIRECT, LOAD_DIRECT_N, R>(plan, spec, a, stream);
+    return launch_cfg<Small16, LOAD_DIRECT, LOAD_DIRECT_N, R>(plan, spec, a, stream);
   }
   if (spec.mx) {
     // MX operands take the DMA loader only (checked by the caller).
     if (!direct) return hipErrorInvalidValue;
     if (plan.bm == 256 && plan.bn == 256)
-      return launch_cfg<Big8X, LOAD_DIRECT, LOAD_DIRECT, false>(plan, spec, a, stream);
+      return launch_cfg<Big8X, LOAD_DIRECT, LOAD_DIRECT, R, false>(plan, spec, a, stream);
     if (plan.bm == 256)
-      return launch_cfg<Mid8X, LOAD_DIRECT, LOAD_DIRECT, false>(plan, spec, a, stream);
-    return launch_cfg<Small8X, LOAD_DIRECT, LOAD_DIRECT, false>(plan, spec, a, stream);
+      return launch_cfg<Mid8X, LOAD_DIRECT, LOAD_DIRECT, R, false>(plan, spec, a, stream);
+    return launch_cfg<Small8X, LOAD_DIRECT, LOAD_DIRECT, R, false>(plan, spec, a, stream);
   }
   if (!direct) {
     // Register loading runs on the 128x128 tile only.
-    if (spec.fp8) return launch_cfg<Small8, LOAD_GENERIC, LOAD_GENERIC>(plan, spec, a, stream);
+    if (spec.fp8) {
+      if constexpr (R) return hipErrorInvalidValue;
+      else return launch_cfg<Small8, LOAD_GENERIC, LOAD_GENERIC, R>(plan, spec, a, stream);
+    }
     if (spec.loader_a == LOAD_DIRECT)
-      return launch_cfg<Small16, LOAD_DIRECT, LOAD_GENERIC>(plan, spec, a, stream);
+      return launch_cfg<Small16, LOAD_DIRECT, LOAD_GENERIC, R>(plan, spec, a, stream);
     if (spec.loader_b == LOAD_DIRECT)
-      return launch_cfg<Small16, LOAD_GENERIC, LOAD_DIRECT>(plan, spec, a, stream);
-    return launch_cfg<Small16, LOAD_GENERIC, LOAD_GENERIC>(plan, spec, a, stream);
+      return launch_cfg<Small16, LOAD_GENERIC, LOAD_DIRECT, R>(plan, spec, a, stream);
+    if constexpr (R) return hipErrorInvalidValue;
+    else return launch_cfg<Small16, LOAD_GENERIC, LOAD_GENERIC, R>(plan, spec, a, stream);
   }
   if (plan.bm == 256 && plan.bn == 256)
-    return spec.fp8 ? launch_cfg<Big8, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream)
-                    : launch_cfg<Big16, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream);
+    return spec.fp8 ? launch_cfg<Big8, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream)
+                    : launch_cfg<Big16, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream);
   if (plan.bm == 256 && plan.bn == 128)
-    return spec.fp8 ? launch_cfg<Mid8, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream)
-                    : launch_cfg<Mid16, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream);
-  return spec.fp8 ? launch_cfg<Small8, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream)
-                  : launch_cfg<Small16, LOAD_DIRECT, LOAD_DIRECT>(plan, spec, a, stream);
+    return spec.fp8 ? launch_cfg<Mid8, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream)
+                    : launch_cfg<Mid16, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream);
+  return spec.fp8 ? launch_cfg<Small8, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream)
+                  : launch_cfg<Small16, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream);
+}
+
+#ifdef G355_TILE_RAGGED
+hipError_t launch_tile_ragged(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
+                              hipStream_t stream) {
+  return launch_tile_t<true>(plan, spec, args, stream);
+}
+#else
+hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
+                       hipStream_t stream) {
+  return spec.ragged ? launch_tile_ragged(plan, spec, args, stream)
+                     : launch_tile_t<false>(plan, spec, args, stream);
 }
 
 template <bool FP8>
@@ -1059,6 +1119,7 @@ hipError_t launch_splitk_reduce(const Plan& plan, const LaunchSpec& spec, const 
                               : launch_reduce<false>(spec, a, stream);
 }
 
+#endif  // G355_TILE_RAGGED
 #endif  // G355_KERNELS_ONLY
 
 }  // namespace g355

@@ -38,11 +38,15 @@ struct LaunchSpec {
   bool a_kmajor, b_kmajor; // layout of each operand (true = K contiguous)
   int out;                 // OutKind
   bool mx;                 // FP8 with E8M0 block scales (GemmArgs::mx_a / mx_b)
+  bool ragged;             // K not a multiple of the 16-byte chunk, a K-major operand DMA-fed
 };
 
 // Enqueue the kernels of a plan. Returns the HIP error of the launch(es).
 hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
                        hipStream_t stream);
+// The same, for spec.ragged (instantiated in a translation unit of its own).
+hipError_t launch_tile_ragged(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
+                              hipStream_t stream);
 hipError_t launch_skinny(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
                          hipStream_t stream);
 hipError_t launch_splitk_reduce(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
