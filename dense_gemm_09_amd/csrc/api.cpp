@@ -190,9 +190,9 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   // The DMA loader addresses an operand with 32-bit byte offsets from its base
   // and marks chunks past K with an offset just beyond the operand's extent:
   // the extent must stay under 2 GiB. K need not be a multiple of the 16-byte
-  // chunk (the kernel writes each row's last, partial chunk itself). Rows are
-  // 16-byte aligned, or, for BF16, at any 2-byte alignment (buffer loads take
-  // unaligned addresses; byte-aligned E4M3 rows go through the register loader).
+  // chunk (the kernel writes each row's last, partial chunk itself), and rows
+  // need not be 16-byte aligned: the buffer loads take any byte offset (BF16
+  // elements must still be 2-byte aligned).
   const int64_t es = fp8 ? 1 : 2;
   const auto under2g = [&](int64_t rows, int64_t ld) {
     return ((rows - 1) * ld + K) * es < (int64_t{1} << 31);
@@ -200,7 +200,7 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   const auto rows16 = [&](const void* p, int64_t ld) { return aligned16(p) && ld % ce == 0; };
   const auto dma_ok = [&](bool kmajor, const void* p, int64_t ld, int64_t rows) {
     const bool even = (reinterpret_cast<uintptr_t>(p) & 1u) == 0;
-    return kmajor && under2g(rows, ld) && (rows16(p, ld) || (!fp8 && even));
+    return kmajor && under2g(rows, ld) && (fp8 || even);
   };
   spec.loader_a = dma_ok(spec.a_kmajor, A, lda, M) ? LOAD_DIRECT : LOAD_GENERIC;
   spec.loader_b = dma_ok(spec.b_kmajor, B, ldb, N) ? LOAD_DIRECT : LOAD_GENERIC;

@@ -123,8 +123,9 @@ gemm_status gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, float alpha,
  * ldsa, ldsb: >= ceil(K/32), multiples of 4, >= 4; the arrays must span
  * M * ldsa and N * ldsb bytes, 4-byte aligned. Bytes past ceil(K/32) in a
  * row are never used.
- * A, B: rows 16-byte aligned (base and ld multiples of 16) and K a multiple of
- * 16, otherwise GEMM_ERR_UNSUPPORTED (the path reads its operands by DMA only).
+ * A, B: any byte alignment and any K; the path reads its operands by DMA
+ * only, with 32-bit offsets, so an operand spanning 2^31 bytes or more
+ * ((rows - 1) * ld + K) gives GEMM_ERR_UNSUPPORTED.
  * There are no FP32 per-token / per-channel scales on this call. Epilogue,
  * C, bias, act, beta, workspace (size: gemm_workspace_size(M, N, K, 1)) and
  * stream as for gemm_fp8_scaled. Errors as for gemm_fp8_scaled, plus
@@ -216,10 +217,12 @@ gemm_status gemm_quantize_fp8_rows(int64_t M, int64_t K, const void* X, int64_t 
  * with leading dimension ldbp. The FP8 DeepGEMM page (sec. 3.2) rearranges B
  * once, before the calls that reuse it, so the reorder is paid once per
  * weight. Pass the result to gemm_bf16 / gemm_fp8_scaled / gemm_mxfp8 with
- * layout_b = GEMM_COL_MAJOR and ldb = ldbp; with ldbp * elem_bytes a multiple
- * of 16, K * elem_bytes a multiple of 16 and Bp 16-byte aligned, B is then
- * copied to on-chip memory by DMA (the fast path) instead of through
- * registers.
+ * layout_b = GEMM_COL_MAJOR and ldb = ldbp: a K-major B (below 2^31 bytes)
+ * is copied to on-chip memory by DMA (the fast path) at any alignment, while
+ * an N-contiguous B is read through registers, several times slower, unless
+ * it is BF16 with 16-byte aligned rows and N a multiple of 8. With ldbp *
+ * elem_bytes and K * elem_bytes multiples of 16 and Bp 16-byte aligned, the
+ * DMA reads are aligned and decode-sized M can use the skinny kernel.
  * B: device, elements of elem_bytes (2: BF16, 1: E4M3; moved as bits), in
  * layout_b (ROW: b(k,n) = B[k*ldb + n], ldb >= N; COL: B[n*ldb + k],
  * ldb >= K). Bp: device, N rows of ldbp >= K elements; the elements k >= K of

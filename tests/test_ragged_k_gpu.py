@@ -1,11 +1,12 @@
 """K that is not a multiple of the 16-byte chunk, on the DMA-fed tile kernels.
 
 K-major operands reach LDS by DMA also when K ends inside a 16-byte chunk
-(8 BF16 / 16 E4M3 elements) and, for BF16, when rows are not 16-byte aligned
-(tight leading dimension such as lda = K = 4093, or a base pointer two bytes
-off). The DMA copies only chunks that lie wholly below the end of K; in the
-last K slice the kernel writes each row's straddling chunk itself (its valid
-elements, then zeros). These tests pin that path against the oracle:
+(8 BF16 / 16 E4M3 elements) and when rows are not 16-byte aligned (tight
+leading dimension such as lda = K = 4093, or a base pointer a few bytes off;
+BF16 at 2-byte, E4M3 at any byte alignment). The DMA copies only chunks that
+lie wholly below the end of K; in the last K slice the kernel writes each
+row's straddling chunk itself (its valid elements, then zeros). These tests
+pin that path against the oracle:
 
 * integer operands, so every summation order is exact and the FP32 output
   must equal the oracle bit for bit;
@@ -62,15 +63,18 @@ def test_bf16_ragged_k_exact(M, N, K, lda, ldb):
     _exact(p, rows)
 
 
-# E4M3 rows must be 16-byte aligned for the DMA (byte-aligned rows take the
-# register loader), so the leading dimensions are multiples of 16.
 FP8_CASES = [
-    (300, 260, 5, 16, 32),         # K inside the first chunk
+    (300, 260, 5, 16, 32),         # K inside the first chunk, padded
+    (300, 260, 5, 5, 5),           # ... tight: byte-aligned rows
     (300, 260, 77, 80, 96),        # K inside the first slice
+    (300, 260, 77, 77, 77),
     (512, 512, 203, 208, 224),     # 256x128
+    (512, 512, 203, 203, 203),
     (520, 600, 129, 144, 144),     # one element past a slice
     (3000, 3000, 203, 208, 208),   # 256x256
+    (3000, 3000, 203, 203, 203),
     (64, 4096, 2053, 2064, 2064),  # split-K
+    (64, 4096, 2053, 2053, 2053),
 ]
 
 
@@ -101,31 +105,43 @@ def test_bf16_ragged_k_random_epilogue(c_dtype):
     compare(p, run(p))
 
 
-def test_bf16_unaligned_base_ragged_k():
-    """Base pointers two bytes past 16-byte alignment and an odd row pitch."""
+def _shifted(t, elems, torch):
+    """A copy of device tensor t starting `elems` elements into a fresh buffer."""
+    buf = torch.zeros(t.numel() + 16, dtype=t.dtype, device="cuda")
+    buf[elems:elems + t.numel()] = t.reshape(-1)
+    return buf, buf.data_ptr() + elems * t.element_size()
+
+
+@pytest.mark.parametrize("kind,shift", [("bf16", 1), ("fp8", 1), ("fp8", 3), ("mxfp8", 5)])
+def test_unaligned_base_ragged_k(kind, shift):
+    """Base pointers `shift` elements past 16-byte alignment and odd row pitches."""
     import torch
     M, N, K = 150, 140, 203
-    p = synth.make_problem("bf16", M, N, K, seed_base=0x750000, int_range=(-4, 4),
-                           c_dtype=OUT_F32)
+    if kind == "mxfp8":
+        p = make_mx_problem(M, N, K, seed_base=0x750000, int_data=(-4, 4),
+                            scale_codes=(126, 129), name="mx_unaligned")
+    else:
+        p = synth.make_problem(kind, M, N, K, seed_base=0x750000 + shift,
+                               int_range=(-4, 4) if kind == "bf16" else (-16, 16),
+                               c_dtype=OUT_F32)
     d = to_device(p)
-    A2 = torch.zeros(p.A.size + 8, dtype=d["A"].dtype, device="cuda")
-    A2[1:1 + p.A.size] = d["A"].reshape(-1)
-    B2 = torch.zeros(p.B.size + 8, dtype=d["B"].dtype, device="cuda")
-    B2[1:1 + p.B.size] = d["B"].reshape(-1)
-    print(f"[gpu] unaligned ragged bf16 M={M} N={N} K={K}", flush=True)
+    keep_a, d["A"] = _shifted(d["A"], shift, torch)
+    keep_b, d["B"] = _shifted(d["B"], shift + 2, torch)
+    print(f"[gpu] unaligned ragged {kind} M={M} N={N} K={K} shift={shift}", flush=True)
     sys.stdout.flush()
-    d["A"], d["B"] = A2.data_ptr() + 2, B2.data_ptr() + 2
     call(p, d)
     torch.cuda.synchronize()
     _, ref = reference(p)
-    assert np.array_equal(d["C"].cpu().numpy(), ref)
+    out = d["C"].cpu().numpy()[:, :N]
+    assert np.array_equal(out, ref), f"{int((out != ref).sum())} mismatches"
 
 
-@pytest.mark.parametrize("M,N,K,lda", [(300, 260, 100, 112), (256, 256, 4093, 4096)])
+@pytest.mark.parametrize("M,N,K,lda", [(300, 260, 100, 112), (300, 260, 100, 100),
+                                       (256, 256, 4093, 4096), (256, 256, 4093, 4093)])
 def test_mx_ragged_k_exact(M, N, K, lda):
     ldsa = max(4, -(-((K + 31) // 32) // 4) * 4)
     p = make_mx_problem(M, N, K, seed_base=0x760000 + K, lda=lda, ldb=lda, ldsa=ldsa, ldsb=ldsa,
-                        int_data=(-4, 4), scale_codes=(126, 129), name=f"mx_ragged_{K}")
+                        int_data=(-4, 4), scale_codes=(126, 129), name=f"mx_ragged_{K}_{lda}")
     _exact(p)
 
 
