@@ -881,19 +881,20 @@ gemm_tile_kernel(GemmArgs p) {
     for (int j = 0; j < SFN; ++j) mxb[j] = ((mxb_raw[j] & keep) | fill) >> (8 * half);
   };
 
-  auto boundary = [&](int j) {
+  // PATCH: this boundary publishes the last slice (nk - 1) of a ragged K range.
+  auto boundary = [&](auto patch, int j) {
     commit((j + C::STAGES - 1) % C::STAGES);
     wait_loads_and_barrier<DMA_BEHIND>();
-    if constexpr (RAGGED) {
-      if (ragged && j + 1 == nk - 1) patch_tail((j + 1) % C::STAGES);
+    if constexpr (decltype(patch)::value) {
+      if (ragged) patch_tail((j + 1) % C::STAGES);
     }
     if constexpr (ALL_DMA) dma_part(Part0{}, j + C::STAGES);
     else fetch(j % C::STAGES, k_begin + (j + C::STAGES) * C::BKE);
   };
-  auto step = [&](int j, int t, const Frag (&ca)[C::FM], const Frag (&cb)[C::FN],
+  auto step = [&](auto patch, int j, int t, const Frag (&ca)[C::FM], const Frag (&cb)[C::FN],
                   Frag (&na)[C::FM], Frag (&nb)[C::FN]) {
     if (t == C::KSTEPS - 1) {
-      boundary(j);
+      boundary(patch, j);
       reads((j + 1) % C::STAGES, 0, na, nb);
       mfmas(ca, cb, t);
       if constexpr (C::MX) mx_ready(j + 1);
@@ -938,14 +939,35 @@ gemm_tile_kernel(GemmArgs p) {
     // U = 2 and nk odd the last pass runs on slice nk, whose loads read zeros:
     // it adds exact zeros.
     constexpr int U = C::KSTEPS % 2 == 0 ? 1 : 2;
-    for (int j0 = 0; j0 < nk; j0 += U) {
+    // Ragged K: the last two slices run after the loop, so that the tail
+    // patch (at the boundary that opens slice nk - 1) stays out of the loop
+    // body and its register allocation.
+    static_assert(!RAGGED || U == 1, "peeled slices assume one slice per pass");
+    const int n_loop = (RAGGED && nk >= 2) ? nk - 2 : nk;
+    for (int j0 = 0; j0 < n_loop; j0 += U) {
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int t = 0; t < C::KSTEPS; ++t) {
-          if (((u * C::KSTEPS + t) & 1) == 0) step(j0 + u, t, fa0, fb0, fa1, fb1);
-          else step(j0 + u, t, fa1, fb1, fa0, fb0);
+          if (((u * C::KSTEPS + t) & 1) == 0)
+            step(std::false_type{}, j0 + u, t, fa0, fb0, fa1, fb1);
+          else
+            step(std::false_type{}, j0 + u, t, fa1, fb1, fa0, fb0);
         }
+    }
+    if constexpr (RAGGED) {
+      if (nk >= 2) {
+#pragma unroll
+        for (int t = 0; t < C::KSTEPS; ++t) {
+          if ((t & 1) == 0) step(std::true_type{}, nk - 2, t, fa0, fb0, fa1, fb1);
+          else step(std::true_type{}, nk - 2, t, fa1, fb1, fa0, fb0);
+        }
+#pragma unroll
+        for (int t = 0; t < C::KSTEPS; ++t) {
+          if ((t & 1) == 0) step(std::false_type{}, nk - 1, t, fa0, fb0, fa1, fb1);
+          else step(std::false_type{}, nk - 1, t, fa1, fb1, fa0, fb0);
+        }
+      }
     }
   }
 
