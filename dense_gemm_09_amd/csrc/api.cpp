@@ -39,6 +39,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
+// Rows up to which the 64-row tile is used.
+constexpr int64_t kThinMaxM = 64;
+
 // Tile-kernel plan (any M): tile shape and split from the cost model.
 static Plan make_tile_plan(int64_t M, int64_t N, int64_t K, bool fp8) {
   const int bke = fp8 ? 128 : 64;
@@ -79,6 +82,41 @@ static Plan make_tile_plan(int64_t M, int64_t N, int64_t K, bool fp8) {
     }
   }
   if (K == 0) best.k_split_len = bke;
+  // Few rows: 64-row tiles with deep rings. They stream B and are bound by
+  // HBM, so the width (256 or 128 columns) and the K split are chosen from
+  // bytes: B spread over the workgroups that run at once (one per CU), plus,
+  // when split, the FP32 partial sums written and read back and the
+  // reduction's launch.
+  if (M <= kThinMaxM) {
+    const double es = fp8 ? 1.0 : 2.0;
+    const double b_time = static_cast<double>(N) * K * es / hbm;
+    double thin_t = 1e30;
+    for (const int bn : {256, 128}) {
+      const int64_t tiles = ceil_div(N, bn);
+      for (int64_t s = 1; s <= 16; ++s) {
+        if (s > 1 && (K == 0 || s > kslices)) break;
+        const int64_t slices_per_split = ceil_div(kslices, s);
+        if (ceil_div(kslices, slices_per_split) != s) continue;  // non-empty partitions
+        const int64_t wgs = tiles * s;
+        if (s > 1 && wgs > kCUs) break;
+        const double fill = static_cast<double>(ceil_div(wgs, kCUs) * kCUs) / wgs;
+        double t = b_time * fill;
+        if (s > 1) t += 2.0 * s * static_cast<double>(M) * N * 4 / hbm + reduce_launch;
+        if (t < thin_t * 0.98) {
+          thin_t = t;
+          best.kernel = KERNEL_TILE;
+          best.bm = 64;
+          best.bn = bn;
+          best.bk = bke;
+          best.waves = bn == 256 ? 4 : 2;
+          best.split = static_cast<int>(s);
+          best.k_split_len = static_cast<int>(slices_per_split * bke);
+          best.grid = wgs;
+          best.workspace = s > 1 ? static_cast<size_t>(s) * M * N * sizeof(float) : 0;
+        }
+      }
+    }
+  }
   return best;
 }
 

@@ -1054,6 +1054,17 @@ using Small8 = TileCfg<128, 128, 2, 2, true, 128, 2>;
 using Big8X = TileCfg<256, 256, 2, 4, true, 128, 2, 2, true>;
 using Mid8X = TileCfg<256, 128, 4, 2, true, 128, 2, 2, true>;
 using Small8X = TileCfg<128, 128, 2, 2, true, 128, 2, 1, true>;
+// Few rows (M <= 64): 64x256 tiles, four waves of 64x64, and a ring of four
+// slices (160 KB). Such a tile does little MFMA work per slice, so it is the
+// memory latency that must be covered: three slices in flight instead of one.
+// 64x128 (two waves of 64x64, six slices, 144 KB) for narrow N, where the
+// wider tile would need a deep K split.
+using Thin16 = TileCfg<64, 256, 1, 4, false, 128, 4>;
+using Thin8 = TileCfg<64, 256, 1, 4, true, 128, 4>;
+using Thin8X = TileCfg<64, 256, 1, 4, true, 128, 4, 1, true>;
+using Narrow16 = TileCfg<64, 128, 1, 2, false, 128, 6>;
+using Narrow8 = TileCfg<64, 128, 1, 2, true, 128, 6>;
+using Narrow8X = TileCfg<64, 128, 1, 2, true, 128, 6, 1, true>;
 
 // The launches of launch_tile, with the kernels' RAGGED flag R. Register
 // loading of both operands has no ragged variant (it bounds every element).
@@ -1067,6 +1078,10 @@ static hipError_t launch_tile_t(const Plan& plan, const LaunchSpec& spec, const 
   if (spec.loader_b == LOAD_DIRECT_N) {
     // BF16, K-major A by DMA, N-contiguous B by DMA (checked by the caller).
     if (spec.fp8 || spec.loader_a != LOAD_DIRECT) return hipErrorInvalidValue;
+    if (plan.bm == 64)
+      return plan.bn == 256
+                 ? launch_cfg<Thin16, LOAD_DIRECT, LOAD_DIRECT_N, R>(plan, spec, a, stream)
+                 : launch_cfg<Narrow16, LOAD_DIRECT, LOAD_DIRECT_N, R>(plan, spec, a, stream);
     if (plan.bm == 256 && plan.bn == 256)
       return launch_cfg<Big16, LOAD_DIRECT, LOAD_DIRECT_N, R>(plan, spec, a, stream);
     if (plan.bm == 256 && plan.bn == 128)
@@ -1076,6 +1091,10 @@ static hipError_t launch_tile_t(const Plan& plan, const LaunchSpec& spec, const 
   if (spec.mx) {
     // MX operands take the DMA loader only (checked by the caller).
     if (!direct) return hipErrorInvalidValue;
+    if (plan.bm == 64)
+      return plan.bn == 256
+                 ? launch_cfg<Thin8X, LOAD_DIRECT, LOAD_DIRECT, R, false>(plan, spec, a, stream)
+                 : launch_cfg<Narrow8X, LOAD_DIRECT, LOAD_DIRECT, R, false>(plan, spec, a, stream);
     if (plan.bm == 256 && plan.bn == 256)
       return launch_cfg<Big8X, LOAD_DIRECT, LOAD_DIRECT, R, false>(plan, spec, a, stream);
     if (plan.bm == 256)
@@ -1095,6 +1114,12 @@ static hipError_t launch_tile_t(const Plan& plan, const LaunchSpec& spec, const 
     if constexpr (R) return hipErrorInvalidValue;
     else return launch_cfg<Small16, LOAD_GENERIC, LOAD_GENERIC, R>(plan, spec, a, stream);
   }
+  if (plan.bm == 64 && plan.bn == 256)
+    return spec.fp8 ? launch_cfg<Thin8, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream)
+                    : launch_cfg<Thin16, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream);
+  if (plan.bm == 64)
+    return spec.fp8 ? launch_cfg<Narrow8, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream)
+                    : launch_cfg<Narrow16, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream);
   if (plan.bm == 256 && plan.bn == 256)
     return spec.fp8 ? launch_cfg<Big8, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream)
                     : launch_cfg<Big16, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream);

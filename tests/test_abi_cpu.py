@@ -123,7 +123,9 @@ def test_workspace_size_of_bad_sizes_is_zero():
 @pytest.mark.parametrize("fp8_", [False, True])
 @pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (4096, 7168, 2048), (512, 4096, 14336),
                                    (8192, 14336, 4096), (1, 4096, 4096), (64, 18432, 4096),
-                                   (4093, 4093, 4093), (256, 256, 256), (1, 1, 1), (5, 7, 0)])
+                                   (4093, 4093, 4093), (256, 256, 256), (1, 1, 1), (5, 7, 0),
+                                   (64, 4096, 4096), (33, 11008, 4096), (17, 100, 333),
+                                   (64, 65536, 4096)])
 def test_plans_are_consistent(M, N, K, fp8_):
     p = g.plan(M, N, K, fp8_)
     assert p.split_k >= 1
@@ -134,9 +136,12 @@ def test_plans_are_consistent(M, N, K, fp8_):
         return
     assert M > 16
     assert p.tile_k == (128 if fp8_ else 64)
-    assert p.tile_m in (128, 256) and p.tile_n in (128, 256)
+    assert (p.tile_m, p.tile_n) in ((128, 128), (256, 128), (256, 256), (64, 256), (64, 128))
     tiles = -(-M // p.tile_m) * -(-N // p.tile_n)
     assert p.grid == tiles * p.split_k
+    if M <= 64:  # a 64-row tile, split to fill the 256 CUs at most once
+        assert p.tile_m == 64 and p.tile_n in (128, 256)
+        assert p.split_k == 1 or p.grid <= 256
     assert p.workspace_bytes == (p.split_k * M * N * 4 if p.split_k > 1 else 0)
     if K == 0:
         assert p.split_k == 1
