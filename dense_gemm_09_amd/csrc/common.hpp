@@ -13,7 +13,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define G355_LDS __attribute__((address_space(3)))
-#define G355_GLOBAL __attribute__((address_space(1)))
 
 enum Act : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_ERF = 2, ACT_GELU_TANH = 3 };
 

@@ -16,17 +16,19 @@
 //   every 8 and every 16 consecutive lanes, so they are conflict-free whether
 //   the LDS serves 128 or 256 bytes of a 128-bit read per cycle.
 // * STAGES slices are in flight in a ring of LDS buffers. K-major operands
-//   with 16-byte aligned rows are copied global -> LDS by global_load_lds_dwordx4
+//   (any row alignment) are copied global -> LDS by buffer_load_dwordx4 ... lds
 //   (64 lanes x 16 B into one contiguous 1 KB segment per instruction). The
 //   lane that lands on physical chunk p of row r fetches logical chunk
 //   p ^ swz(r), so the swizzle costs nothing and no VGPRs hold staged data.
-//   Chunks at or past K read a 16-byte block of zeros; rows past M (or N) read
-//   a clamped valid row whose results are never stored. Every iteration issues
-//   the same number of DMA instructions (slices past the end read zeros), so
-//   waiting for the oldest slice is a fixed vmcnt.
-// * Other operands (B row-major, A column-major, or rows that are not 16-byte
-//   aligned) are loaded element-wise into registers and written to the same
-//   swizzled layout after the slice's MFMAs.
+//   Chunks that do not end before the end of K read zeros through the buffer
+//   range check; a chunk that straddles it is written by patch_tail; rows
+//   past M (or N) read a clamped valid row whose results are never stored.
+//   Every iteration issues the same number of DMA instructions (slices past
+//   the end read zeros), so waiting for the oldest slice is a fixed vmcnt.
+// * A BF16 B stored N-contiguous is copied the same way into an N-major tile
+//   (NmajorLoader). Other operands (A column-major, an E4M3 B row-major,
+//   operands of 2 GiB or more) are loaded element-wise into registers and
+//   written to the same swizzled layout after the slice's MFMAs.
 // * BF16 uses v_mfma_f32_32x32x16_bf16; FP8 uses v_mfma_scale_f32_32x32x64_f8f6f4
 //   with the E4M3 format code and the neutral block scale 2^0 (E8M0 code 127).
 //   The per-token / per-channel scales are FP32 and applied in the epilogue.
