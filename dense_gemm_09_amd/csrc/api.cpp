@@ -55,7 +55,7 @@ static Plan make_tile_plan(int64_t M, int64_t N, int64_t K, bool fp8) {
   double best_t = 1e30;
   for (const Candidate& c : kCandidates) {
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
-    for (int s = 1; s <= 16; s *= 2) {
+    for (int s = 1; s <= kMaxSplit; s *= 2) {
       if (s > 1 && (K == 0 || s > kslices)) break;
       const int64_t slices_per_split = ceil_div(kslices, s);
       const int64_t splits = ceil_div(kslices, slices_per_split);  // non-empty partitions
@@ -93,7 +93,7 @@ static Plan make_tile_plan(int64_t M, int64_t N, int64_t K, bool fp8) {
     double thin_t = 1e30;
     for (const int bn : {256, 128}) {
       const int64_t tiles = ceil_div(N, bn);
-      for (int64_t s = 1; s <= 16; ++s) {
+      for (int64_t s = 1; s <= kMaxSplit; ++s) {
         if (s > 1 && (K == 0 || s > kslices)) break;
         const int64_t slices_per_split = ceil_div(kslices, s);
         if (ceil_div(kslices, slices_per_split) != s) continue;  // non-empty partitions

@@ -992,8 +992,16 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs p) {
   if (idx >= MN) return;
   const int m = static_cast<int>(idx / p.N);
   const int n = static_cast<int>(idx - static_cast<int64_t>(m) * p.N);
+  // All partials are loaded before the first add (one memory round trip
+  // instead of split_k dependent ones), then summed in split order.
+  float part[kMaxSplit];
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s)
+    if (s < p.split_k) part[s] = p.workspace[s * MN + idx];
   float v = 0.f;
-  for (int s = 0; s < p.split_k; ++s) v += p.workspace[s * MN + idx];
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s)
+    if (s < p.split_k) v += part[s];
   if constexpr (FP8) v = v * (p.scale_a[m] * p.scale_b[n]);
   v = p.alpha * v;
   const int64_t off = static_cast<int64_t>(m) * p.ldc + n;

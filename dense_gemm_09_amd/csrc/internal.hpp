@@ -32,6 +32,10 @@ struct Plan {
 // Chooses the kernel, tile and split for a shape (host arithmetic only).
 Plan make_plan(int64_t M, int64_t N, int64_t K, bool fp8);
 
+// Largest K split a plan uses (the reduction kernel holds that many partials
+// per thread).
+constexpr int kMaxSplit = 16;
+
 struct LaunchSpec {
   bool fp8;
   int loader_a, loader_b;  // Loader
