@@ -49,6 +49,18 @@ def test_thin_tile_row_major_b_exact(N):
     _exact(p)
 
 
+@pytest.mark.parametrize("la,lb", [(1, 1), (1, 0), (0, 0)])
+def test_few_rows_register_loaded_operands_exact(la, lb):
+    """M <= 64 with an operand the DMA path cannot read (A column-major, or a
+    row-major B whose N is not a multiple of 8): the 128x128 register-loader
+    tile runs with the K split planned for the 64-row tile."""
+    M, N, K = 40, 300 if lb == 1 else 301, 3001
+    p = synth.make_problem("bf16", M, N, K, seed_base=0x7A0000 + la * 2 + lb, layout_a=la,
+                           layout_b=lb, int_range=(-4, 4), c_dtype=OUT_F32)
+    assert g.plan(M, N, K, False).split_k > 1
+    _exact(p)
+
+
 @pytest.mark.parametrize("kind,c_dtype,act", [("bf16", OUT_BF16, ACT_GELU_ERF),
                                               ("bf16", OUT_F32, ACT_RELU),
                                               ("fp8", OUT_BF16, ACT_GELU_ERF)])
