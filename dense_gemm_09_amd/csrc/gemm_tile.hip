@@ -401,12 +401,16 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
       if (m >= M) continue;
       const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
       if (vec_ok) {
+        // C_in is read once (non-temporal, like the stores of C).
         if constexpr (OUT == OUT_BF16) {
-          const uint2 h = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.C) + off);
+          const u32x2 h = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.C) + off));
           dst[it] = make_float4(__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xffff0000u),
                                 __uint_as_float(h.y << 16), __uint_as_float(h.y & 0xffff0000u));
         } else {
-          dst[it] = *reinterpret_cast<const float4*>(static_cast<const float*>(p.C) + off);
+          const f32x4 c = __builtin_nontemporal_load(
+              reinterpret_cast<const f32x4*>(static_cast<const float*>(p.C) + off));
+          dst[it] = make_float4(c[0], c[1], c[2], c[3]);
         }
       } else {
         float t[4] = {0.f, 0.f, 0.f, 0.f};
