@@ -493,13 +493,14 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
       if (m >= M) continue;
       float v[4] = {a4.x, a4.y, a4.z, a4.w};
       if constexpr (SPLIT) {
+        // Partials are written once and read once by the reduction: non-temporal.
         float* w = p.workspace + (static_cast<int64_t>(split) * M + m) * N + n;
         if (vec_ok && (N & 3) == 0) {
-          *reinterpret_cast<float4*>(w) = a4;
+          __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(w));
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            if (n + q < N) w[q] = v[q];
+            if (n + q < N) __builtin_nontemporal_store(v[q], w + q);
         }
         continue;
       } else {
