@@ -105,11 +105,11 @@ __device__ __forceinline__ void store_out1(void* C, int64_t off, float v, float 
 }
 
 // Elements off..off+3 in one store (16, 8 or 4 bytes, aligned by the caller).
-template <int OUT>
 // The stores are non-temporal: C is written once at the end of a tile and not
 // read again by the kernel, so it need not displace A and B panels from the
 // caches (measured at 4096^3 together with non-temporal C_in loads: ~5% off
 // the BF16 and the FP8 kernel).
+template <int OUT>
 __device__ __forceinline__ void store_out4(void* C, int64_t off, const float (&v)[4], float s,
                                            float zp) {
   if constexpr (OUT == OUT_F32) {
