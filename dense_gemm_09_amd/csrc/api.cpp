@@ -32,14 +32,15 @@ struct Candidate {
 // The efficiencies rank the candidates rather than predict time. For BF16 the
 // 256x128 and 128x128 figures sit below 0.68 so that a 256x256 tile split two
 // ways wins where it fills the chip (M = 2048, N = 4096, K = 14336: 247 us
-// against 300 us for 256x128 tiles unsplit and 278 us for 128x128). FP8's
-// 128x128 tile, two per CU, keeps its matrix cores busier than BF16's: at
-// 1024 x 4096 x 4096 it runs 37 us against 50 us for 256x128 tiles, and at
-// 2048 x 4096 x 14336 131 us against 160 us.
+// against 300 us for 256x128 tiles unsplit and 278 us for 128x128), and
+// 128x128 ranks above 256x128 (two per CU: 512 x 12288 x 4096 80 us against
+// 85 us, 256^3 8.6 us against 10.1 us). FP8's 128x128 tile keeps its matrix
+// cores busier still: at 1024 x 4096 x 4096 it runs 35 us against 46 us for
+// 256x128 tiles, and at 2048 x 4096 x 14336 131 us against 160 us.
 constexpr Candidate kCandidates[] = {
     {256, 256, 8, 1, {0.85, 0.85}},
-    {256, 128, 8, 1, {0.65, 0.65}},
-    {128, 128, 4, 2, {0.65, 0.80}},
+    {256, 128, 8, 1, {0.62, 0.65}},
+    {128, 128, 4, 2, {0.67, 0.80}},
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -14,8 +14,8 @@ pin that path against the oracle:
   K that reached the MFMA shows up as NaN; tight ones, where the elements
   past K of a row are the next row's (nonzero) values;
 * K below one slice (the patched slice is the first), K a few elements past
-  a slice, split-K (only the last split ends inside a chunk), the 256x256,
-  256x128 and 128x128 tiles (the last with one register-loaded operand),
+  a slice, split-K (only the last split ends inside a chunk), the 256x256
+  and 128x128 tiles (the last also with one register-loaded operand),
   N-contiguous B with a DMA-fed ragged A, unaligned base pointers, and MX.
 """
 from __future__ import annotations
@@ -43,10 +43,10 @@ def _exact(p, rows=None):
 
 BF16_CASES = [
     # M, N, K, lda, ldb            tile / what
-    (300, 260, 5, 5, 5),           # 256x128, K inside the first chunk, tight
+    (300, 260, 5, 5, 5),           # 128x128, K inside the first chunk, tight
     (300, 260, 37, 37, 37),        # K inside the first slice, tight (odd row pitch)
     (300, 260, 37, 48, 56),        # ... padded (NaN after K)
-    (512, 512, 203, 203, 203),     # 256x128, four slices, tight
+    (512, 512, 203, 203, 203),     # 128x128, four slices, tight
     (512, 512, 203, 216, 208),     # ... padded
     (520, 600, 65, 65, 72),        # one element past a slice
     (3000, 3000, 203, 203, 203),   # 256x256
@@ -68,7 +68,7 @@ FP8_CASES = [
     (300, 260, 5, 5, 5),           # ... tight: byte-aligned rows
     (300, 260, 77, 80, 96),        # K inside the first slice
     (300, 260, 77, 77, 77),
-    (512, 512, 203, 208, 224),     # 256x128
+    (512, 512, 203, 208, 224),     # 128x128
     (512, 512, 203, 203, 203),
     (520, 600, 129, 144, 144),     # one element past a slice
     (3000, 3000, 203, 208, 208),   # 256x256
@@ -151,4 +151,5 @@ def test_plans_cover_split_and_both_tiles():
     assert g.plan(130, 260, 4093, False).split_k > 1
     assert g.plan(64, 4096, 2053, True).split_k > 1
     assert (g.plan(3000, 3000, 203, False).tile_m, g.plan(3000, 3000, 203, False).tile_n) == (256, 256)
-    assert (g.plan(512, 512, 203, False).tile_m, g.plan(512, 512, 203, False).tile_n) == (256, 128)
+    assert (g.plan(512, 512, 203, False).tile_m, g.plan(512, 512, 203, False).tile_n) == (128, 128)
+    assert (g.plan(512, 512, 203, True).tile_m, g.plan(512, 512, 203, True).tile_n) == (128, 128)
