@@ -156,6 +156,24 @@ def test_square_4096_uses_one_full_wave_of_256_tiles():
     assert (p.tile_m, p.tile_n, p.split_k, p.grid) == (256, 256, 1, 256)
 
 
+# Plans chosen by the tile ranking, each measured on the GPU as the fastest (or
+# within noise of it) among the forced alternatives of tile shape and split.
+@pytest.mark.parametrize("M,N,K,fp8_,want", [
+    (4096, 4096, 4096, True, (256, 256, 1)),
+    (4096, 7168, 2048, True, (256, 256, 1)),
+    (4093, 4093, 4093, False, (256, 256, 1)),
+    (8192, 14336, 4096, False, (256, 256, 1)),
+    (2048, 4096, 14336, False, (256, 256, 2)),
+    (512, 12288, 4096, False, (128, 128, 1)),
+    (512, 4096, 14336, False, (128, 128, 4)),
+    (1024, 4096, 4096, True, (128, 128, 1)),
+    (2048, 4096, 14336, True, (128, 128, 1)),
+])
+def test_measured_plans(M, N, K, fp8_, want):
+    p = g.plan(M, N, K, fp8_)
+    assert (p.tile_m, p.tile_n, p.split_k) == want
+
+
 def test_plan_null_out():
     assert g.lib().gemm_plan(4, 4, 4, 0, None) == NULLP
 
