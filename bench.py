@@ -24,8 +24,10 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK = {"bf16": 2516.6, "fp8": 5033.2}  # TFLOP/s, MI355X dense
-HBM_GBPS = 8000.0
+from dense_gemm_09_amd.roofline import MI355X_HBM_GBPS, MI355X_PEAK_TFLOPS  # noqa: E402
+
+PEAK = {k: MI355X_PEAK_TFLOPS[k] for k in ("bf16", "fp8")}  # TFLOP/s, MI355X dense
+HBM_GBPS = MI355X_HBM_GBPS
 ROTATE_BYTES = 600 << 20  # > 2 x (256 MB MALL + 32 MB L2)
 
 
@@ -89,10 +91,7 @@ def time_calls(fns, steps, warmup):
     """Run the callables in order per step; per-callable mean ms from HIP events."""
     import torch
     s = torch.cuda.current_stream()
-    for _ in range(warmup):
-        for f in fns:
-            f()
-    torch.cuda.synchronize()
+    warm(fns, warmup)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
     t0 = time.perf_counter()
     for k in range(steps):
@@ -108,18 +107,26 @@ def time_calls(fns, steps, warmup):
     return per, total, wall
 
 
+def warm(fns, warmup):
+    """`warmup` untimed calls of each callable, and at least one call on each of
+    its rotating buffer sets, so that no set is first touched while timed."""
+    import torch
+    for f in fns:
+        for _ in range(max(warmup, len(getattr(f, "sets", ())))):
+            f()
+    torch.cuda.synchronize()
+
+
 def time_blocks(fns, steps, warmup):
     """`steps` steps of the callables, run callable by callable: all `steps`
     calls of the first back to back, then of the second, ... (the same work as
-    `steps` interleaved steps). HIP events only at block edges on the current
-    stream, so a per-callable mean (ms) is its kernels' back-to-back time, with
-    no timing packet between launches. Returns (per-callable ms, total ms, wall s)."""
+    `steps` interleaved steps). HIP events only at block edges on the kernels'
+    stream (the current stream, which the calls launch on), so a per-callable
+    mean (ms) is its kernels' back-to-back time, with no timing packet between
+    launches. Returns (per-callable ms, total ms, wall s)."""
     import torch
     s = torch.cuda.current_stream()
-    for f in fns:
-        for _ in range(warmup):
-            f()
-    torch.cuda.synchronize()
+    warm(fns, warmup)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
     t0 = time.perf_counter()
     ev[0].record(s)
@@ -131,6 +138,25 @@ def time_blocks(fns, steps, warmup):
     wall = time.perf_counter() - t0
     per = [ev[j].elapsed_time(ev[j + 1]) / steps for j in range(len(fns))]
     return per, ev[0].elapsed_time(ev[-1]), wall
+
+
+def launch_medians(fns, steps):
+    """Median per-launch time (ms) of each callable: an event pair around every
+    call (after the callables have been warmed by time_blocks)."""
+    import torch
+    s = torch.cuda.current_stream()
+    out = []
+    for f in fns:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, b in ev:
+            a.record(s)
+            f()
+            b.record(s)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        out.append(t[len(t) // 2])
+    return out
 
 
 def time_graph(fn, calls, reps=5):
@@ -160,15 +186,29 @@ def time_graph(fn, calls, reps=5):
     return e0.elapsed_time(e1) / (reps * calls)
 
 
-def cpu_baseline(bf16_p, fp8_p, min_seconds=10.0):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(bf16_p, fp8_p, min_seconds=12.0):
     """The oracle as it stands on the host, on the headline step's own inputs: blocks of
-    1024 rows of the BF16 and of the FP8 4096^3 GEMM, cycling through the rows, until
-    min_seconds have passed (a bounded sample of about 10 s)."""
+    256 rows of the BF16 and of the FP8 4096^3 GEMM (decode from the bit fields,
+    the ascending-k float64 triple loop of oracle/triple_loop.c with OpenMP over rows,
+    the epilogue and the output rounding), cycling through the rows, until
+    min_seconds have passed (a bounded sample)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
     import oracle  # noqa: F401  (the CPU-baseline leg is the one bench path allowed to use it)
+    from oracle import native
     from tests.common import reference
-    block = 1024
+    _, threads = native.accumulate(np.zeros((2, 1)), np.zeros((1, 1)), return_threads=True)
+    block = 256
     flops = 0
     blocks = 0
     t0 = time.perf_counter()
@@ -182,19 +222,28 @@ def cpu_baseline(bf16_p, fp8_p, min_seconds=10.0):
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
-    threads = max((i.get("num_threads", 1) for i in threadpool_info()
-                   if i.get("user_api") == "blas"), default=1)
+    steps = blocks * block / bf16_p.M
     return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
-            "sample": f"{blocks} blocks of 1024 rows of the BF16 and of the FP8 4096^3 GEMM "
-                      f"({blocks / 4:.2f} steps), float64 oracle incl. decode and epilogue, "
-                      f"{dt:.1f} s"}
+            "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "timed": "oracle.gemm_bf16 + oracle.gemm_fp8_scaled: bit-field decode, float64 "
+                     "i-k-j triple loop (oracle/triple_loop.c, OpenMP over output rows), "
+                     "epilogue, output rounding",
+            "sample": f"{blocks} blocks of 256 rows of the BF16 and of the FP8 4096^3 GEMM "
+                      f"({steps:.3f} steps), {dt:.1f} s, {threads} OpenMP threads"}
 
 
 def kernel_source_sha():
+    """Hash of every library source (csrc/*, include/*): a profile taken on
+    another tree does not describe this one."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm_tile.hip", "common.hpp"):
-        with open(os.path.join(ROOT, "dense_gemm_09_amd", "csrc", f), "rb") as fh:
+    files = []
+    for d in (os.path.join(ROOT, "dense_gemm_09_amd", "csrc"), os.path.join(ROOT, "include")):
+        files += sorted(os.path.join(d, f) for f in os.listdir(d)
+                        if f.endswith((".hip", ".hpp", ".cpp", ".h")))
+    for path in files:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -215,19 +264,24 @@ def measured_traffic():
 
 
 def pmc_run(p_bf16, p_fp8):
-    """Known-size copy (calibrates FETCH_SIZE / WRITE_SIZE), then the GEMMs."""
+    """Known-size copy (calibrates FETCH_SIZE / WRITE_SIZE), then the GEMMs over
+    their rotating buffer sets, as in the timed run: every launch after the
+    first round reads operands that are not in the caches."""
     import torch
     src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    w_bf16, w_fp8 = Workload(p_bf16, 1), Workload(p_fp8, 1)
-    for _ in range(3):
+    w_bf16, w_fp8 = Workload(p_bf16, copies_for(p_bf16)), Workload(p_fp8, copies_for(p_fp8))
+    n = 2 * max(len(w_bf16.sets), len(w_fp8.sets))
+    for _ in range(n):
         w_bf16()
+    for _ in range(n):
         w_fp8()
     torch.cuda.synchronize()
-    log("[bench] pmc run done: copy 268435456 bytes, 3 x bf16 4096^3, 3 x fp8 4096^3")
+    log(f"[bench] pmc run done: copy 268435456 bytes, {n} x bf16 4096^3 over "
+        f"{len(w_bf16.sets)} sets, {n} x fp8 4096^3 over {len(w_fp8.sets)} sets")
 
 
 def main():
@@ -259,6 +313,7 @@ def main():
     torch.cuda.synchronize()
     per, total_ms, wall = time_blocks([w_bf16, w_fp8], args.steps, args.warmup)
     torch.cuda.synchronize()
+    med = launch_medians([w_bf16, w_fp8], args.steps)
     ms_step = total_ms / args.steps
     fl_bf16, fl_fp8 = p_bf16.flops, p_fp8.flops
     tf_bf16 = fl_bf16 / (per[0] * 1e-3) / 1e12
@@ -275,9 +330,12 @@ def main():
             "algorithmic_flops_per_launch": fl_bf16, "avg_launch_us": round(per[0] * 1e3, 2)}
 
     extra = {"bf16_4096": {"us": round(per[0] * 1e3, 2), "tflops": round(tf_bf16, 1),
-                           "frac_peak": round(tf_bf16 / PEAK["bf16"], 4)},
+                           "frac_peak": round(tf_bf16 / PEAK["bf16"], 4),
+                           "median_launch_us": round(med[0] * 1e3, 2)},
              "fp8_4096": {"us": round(per[1] * 1e3, 2), "tflops": round(tf_fp8, 1),
-                          "frac_peak": round(tf_fp8 / PEAK["fp8"], 4)}}
+                          "frac_peak": round(tf_fp8 / PEAK["fp8"], 4),
+                          "median_launch_us": round(med[1] * 1e3, 2)},
+             "kernel_source_sha256": kernel_source_sha()}
     del w_bf16, w_fp8
     torch.cuda.empty_cache()
 

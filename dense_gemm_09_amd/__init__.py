@@ -154,11 +154,12 @@ def gemm_bf16(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, beta, C, ldc, 
     """C = act(alpha * A B + beta * C + bias), BF16 inputs, FP32 accumulation.
 
     A, B, C, bias, workspace: device tensors (or raw device addresses as int).
-    With workspace=None a workspace of the required size is allocated here.
+    With workspace=None a workspace of the required size is allocated here, on
+    the stream the call runs on.
     """
     L = lib()
     _check_operands(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, c_dtype, 2, bias)
-    workspace, workspace_bytes = _workspace(M, N, K, False, workspace, workspace_bytes, C)
+    workspace, workspace_bytes = _workspace(M, N, K, False, workspace, workspace_bytes, stream)
     st = L.gemm_bf16(M, N, K, alpha, _ptr(A), lda, layout_a, _ptr(B), ldb, layout_b, beta,
                      _ptr(C), ldc, c_dtype, _ptr(bias), act, _ptr(workspace), workspace_bytes,
                      _stream(stream))
@@ -175,7 +176,7 @@ def gemm_fp8_scaled(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, scale_a,
     if M > 0 and N > 0:
         _need(scale_a, 4 * M, "scale_a")
         _need(scale_b, 4 * N, "scale_b")
-    workspace, workspace_bytes = _workspace(M, N, K, True, workspace, workspace_bytes, C)
+    workspace, workspace_bytes = _workspace(M, N, K, True, workspace, workspace_bytes, stream)
     st = L.gemm_fp8_scaled(M, N, K, alpha, _ptr(A), lda, layout_a, _ptr(B), ldb, layout_b,
                            _ptr(scale_a), _ptr(scale_b), beta, _ptr(C), ldc, c_dtype,
                            _ptr(bias), act, _ptr(workspace), workspace_bytes, _stream(stream))
@@ -193,7 +194,7 @@ def gemm_mxfp8(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, scale_a, ldsa
     if M > 0 and N > 0 and K > 0:
         _need(scale_a, M * ldsa, "scale_a")
         _need(scale_b, N * ldsb, "scale_b")
-    workspace, workspace_bytes = _workspace(M, N, K, True, workspace, workspace_bytes, C)
+    workspace, workspace_bytes = _workspace(M, N, K, True, workspace, workspace_bytes, stream)
     st = L.gemm_mxfp8(M, N, K, alpha, _ptr(A), lda, layout_a, _ptr(B), ldb, layout_b,
                       _ptr(scale_a), ldsa, _ptr(scale_b), ldsb, beta, _ptr(C), ldc, c_dtype,
                       _ptr(bias), act, _ptr(workspace), workspace_bytes, _stream(stream))
@@ -215,7 +216,7 @@ def gemm_bf16_quant(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, bias, ac
     L = lib()
     _check_operands(M, N, K, A, lda, layout_a, B, ldb, layout_b, None, ldq, OUT_BF16, 2, bias)
     _check_quant_out(M, N, Q, ldq, out_scale, out_zero)
-    workspace, workspace_bytes = _workspace(M, N, K, False, workspace, workspace_bytes, Q)
+    workspace, workspace_bytes = _workspace(M, N, K, False, workspace, workspace_bytes, stream)
     st = L.gemm_bf16_quant(M, N, K, alpha, _ptr(A), lda, layout_a, _ptr(B), ldb, layout_b,
                            _ptr(bias), act, _ptr(out_scale), _ptr(out_zero), _ptr(Q), ldq,
                            q_dtype, _ptr(workspace), workspace_bytes, _stream(stream))
@@ -233,7 +234,7 @@ def gemm_fp8_scaled_quant(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, sc
     if M > 0 and N > 0:
         _need(scale_a, 4 * M, "scale_a")
         _need(scale_b, 4 * N, "scale_b")
-    workspace, workspace_bytes = _workspace(M, N, K, True, workspace, workspace_bytes, Q)
+    workspace, workspace_bytes = _workspace(M, N, K, True, workspace, workspace_bytes, stream)
     st = L.gemm_fp8_scaled_quant(M, N, K, alpha, _ptr(A), lda, layout_a, _ptr(B), ldb, layout_b,
                                  _ptr(scale_a), _ptr(scale_b), _ptr(bias), act, _ptr(out_scale),
                                  _ptr(out_zero), _ptr(Q), ldq, q_dtype, _ptr(workspace),
@@ -266,13 +267,28 @@ def quantize_fp8_rows(M, K, X, ldx, Q, ldq, scale, stream=None):
         raise GemmError(st, "gemm_quantize_fp8_rows")
 
 
-def _workspace(M, N, K, fp8, workspace, workspace_bytes, like):
+def _torch_stream(stream):
+    """The torch stream object of a call's `stream` argument (None: current)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.default_stream() if stream == 0 else torch.cuda.ExternalStream(stream)
+    return stream
+
+
+def _workspace(M, N, K, fp8, workspace, workspace_bytes, stream):
     if workspace is None:
         need = workspace_size(M, N, K, fp8) if M >= 0 and N >= 0 and K >= 0 else 0
         if need == 0:
             return None, 0
         import torch
-        workspace = torch.empty(need, dtype=torch.uint8, device=like.device)
+        # Allocated on the stream the kernels run on: torch's caching allocator
+        # then gives the block to a later allocation only in that stream's
+        # order, i.e. after this call's kernels have finished with it.
+        s = _torch_stream(stream)
+        with torch.cuda.stream(s):
+            workspace = torch.empty(need, dtype=torch.uint8, device=s.device)
         return workspace, need
     if workspace_bytes is None:
         workspace_bytes = _nbytes(workspace) if not isinstance(workspace, int) else 0

@@ -15,8 +15,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemm355.so")
-SOURCES = ["api.cpp", "gemm_tile.hip", "gemm_tile_ragged.hip", "gemm_skinny.hip", "quant.hip",
-           "pack.hip"]
+# (source, object name, extra defines). gemm_tile.hip is compiled once per
+# (ragged flag, output part) and once for the split-K reduction, so that its
+# kernel variants build in parallel.
+SOURCES = [("api.cpp", "api", []), ("gemm_skinny.hip", "gemm_skinny", []),
+           ("quant.hip", "quant", []), ("pack.hip", "pack", []),
+           ("gemm_tile.hip", "gemm_reduce", ["-DG355_REDUCE=1"])]
+SOURCES += [("gemm_tile.hip", f"gemm_tile_r{r}_p{p}", [f"-DG355_RAGGED={r}", f"-DG355_PART={p}"])
+            for r in (0, 1) for p in range(5)]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -27,9 +33,10 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS]
+def _compile(item) -> str:
+    src, name, defines = item
+    obj = os.path.join(BUILD, name + ".o")
+    cmd = [HIPCC, *FLAGS, *defines]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -42,9 +49,11 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     """Compile every source and link the shared library. Returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
+    jobs = int(os.environ.get("MAX_JOBS", os.cpu_count() or 8))
+    # the long compiles first
+    order = sorted(SOURCES, key=lambda it: it[0] != "gemm_tile.hip")
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(16, jobs, len(order)))) as ex:
+        objs = list(ex.map(_compile, order))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -149,6 +149,22 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool fp8) {
   return s;
 }
 
+hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
+                       hipStream_t stream) {
+  using Fn = hipError_t (*)(const Plan&, const LaunchSpec&, const GemmArgs&, hipStream_t);
+  static constexpr Fn kParts[2][kOutParts] = {
+      {launch_tile_r0_p0, launch_tile_r0_p1, launch_tile_r0_p2, launch_tile_r0_p3,
+       launch_tile_r0_p4},
+      {launch_tile_r1_p0, launch_tile_r1_p1, launch_tile_r1_p2, launch_tile_r1_p3,
+       launch_tile_r1_p4}};
+  const int part = plan.split > 1        ? PART_SPLIT
+                   : spec.out == OUT_F32  ? PART_F32
+                   : spec.out == OUT_BF16 ? PART_BF16
+                   : spec.out == OUT_I8   ? PART_I8
+                                          : PART_E4M3;
+  return kParts[spec.ragged ? 1 : 0][part](plan, spec, args, stream);
+}
+
 }  // namespace g355
 
 using namespace g355;
@@ -311,7 +327,12 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   a.k_split_len = p.k_split_len;
   a.tiles_m = static_cast<int>((M + p.bm - 1) / p.bm);
   a.tiles_n = static_cast<int>((N + p.bn - 1) / p.bn);
+  a.ws_vec = (reinterpret_cast<uintptr_t>(workspace) & 15u) == 0 ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // hipGetLastError after a launch also returns an error that an earlier,
+  // unrelated HIP call on this thread left pending: consume any such error
+  // first, so that GEMM_ERR_HIP reports this call's own launches only.
+  (void)hipGetLastError();
   if (p.kernel == KERNEL_SKINNY) {
     a.a_mn_major = a.b_mn_major = 0;
     return launch_skinny(p, spec, a, s) == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;

@@ -43,6 +43,7 @@ struct GemmArgs {
   int a_mn_major;         // 1: A stored column-major (M contiguous), read by the generic loader
   int b_mn_major;         // 1: B stored row-major (N contiguous), read by the generic loader
   int c_vec;              // 1: C rows allow 4-element vector access (aligned base, ldc % 4 == 0)
+  int ws_vec;             // 1: the workspace is 16-byte aligned
   int split_k;            // number of K partitions
   int k_split_len;        // elements of K per partition (multiple of the K tile)
   int tiles_m, tiles_n;
@@ -155,36 +156,85 @@ __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
-// erf(x) by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
-// 7.1.26: for x >= 0, erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5)
-// e^(-x^2) with t = 1 / (1 + p x), |error| <= 1.5e-7; odd symmetry for x < 0.
-// About a dozen VALU operations (one hardware exp, one hardware reciprocal)
-// instead of a full-precision library erf.
-__device__ __forceinline__ float erf_as7126(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(1.f + 0.3275911f * ax);
-  float poly = 1.061405429f;
-  poly = poly * t - 1.453152027f;
-  poly = poly * t + 1.421413741f;
-  poly = poly * t - 0.284496736f;
-  poly = poly * t + 0.254829592f;
-  poly = poly * t;
-  const float r = 1.f - poly * fast_exp(-ax * ax);
-  return copysignf(r, x);
+// e^a for a double a, to about one FP32 ulp for any a: a*log2(e) = n + f with
+// n integral and |f| <= 1/2 (both exact in double), 2^f from the hardware
+// exponential, 2^n applied exactly by ldexp. fast_exp loses relative accuracy
+// for large |x| instead (x*log2(e) is rounded to FP32, an absolute error of up
+// to ~4e-6 in the exponent near the FP32 underflow).
+__device__ __forceinline__ float exp_split(double a) {
+  double q = a * 1.4426950408889634074;
+  q = q < -400.0 ? -400.0 : (q > 400.0 ? 400.0 : q);  // past FP32's range either way
+  const double n = __builtin_rint(q);
+  const float r = __builtin_amdgcn_exp2f(static_cast<float>(q - n));
+  return __builtin_ldexpf(r, static_cast<int>(n));
 }
 
+// P(t) of the Chebyshev-fitted complementary error function of Numerical
+// Recipes in C (2nd ed., sec. 6.2, "erfcc"): for x >= 0,
+//   erfc(x) = t exp(-x^2 + P(t)),  t = 1 / (1 + x/2),
+// with a fractional error below 1.2e-7 for every x. Unlike 1 - erf(x), it
+// keeps its relative accuracy where erfc(x) is tiny.
+__device__ __forceinline__ float erfc_cheb_poly(float t) {
+  float p = 0.17087277f;
+  p = fmaf(p, t, -0.82215223f);
+  p = fmaf(p, t, 1.48851587f);
+  p = fmaf(p, t, -1.13520398f);
+  p = fmaf(p, t, 0.27886807f);
+  p = fmaf(p, t, -0.18628806f);
+  p = fmaf(p, t, 0.09678418f);
+  p = fmaf(p, t, 0.37409196f);
+  p = fmaf(p, t, 1.00002368f);
+  p = fmaf(p, t, -1.26551223f);
+  return p;
+}
+
+// GELU(z) = z Phi(z), Phi(z) = erfc(-z / sqrt 2) / 2: Phi(z) = e/2 for z < 0
+// and 1 - e/2 for z >= 0 with e = erfc(|z| / sqrt 2), so the result keeps its
+// relative accuracy on both sides (far into the negative range it is a tiny
+// number, not the difference of two numbers near 1). The exponent -z^2/2 + P
+// is one fused multiply-add from z itself (0.5 z is exact). PRECISE forms it
+// in double and takes e^a by exp_split: relative error ~1e-6 for every z
+// (FP32 outputs); otherwise the FP32 exponent's rounding leaves a relative
+// error of up to ~1e-5 at the far negative end, far below a BF16 ulp.
+template <bool PRECISE>
+__device__ __forceinline__ float gelu_erf(float z) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, x, 1.f));
+  const float p = erfc_cheb_poly(t);
+  float e;
+  if constexpr (PRECISE) {
+    const double zd = z;
+    e = t * exp_split(static_cast<double>(p) - 0.5 * zd * zd);
+  } else {
+    e = t * fast_exp(fmaf(-0.5f * z, z, p));
+  }
+  const float phi = z < 0.f ? 0.5f * e : fmaf(-0.5f, e, 1.f);
+  return z * phi;
+}
+
+// tanh-form GELU: 0.5 z (1 + tanh u) = z / (1 + e^(-2u)), u = sqrt(2/pi)
+// (z + 0.044715 z^3); no cancellation for either sign of z. PRECISE forms u
+// and e^(-2u) in double / by exp_split.
+template <bool PRECISE>
+__device__ __forceinline__ float gelu_tanh(float z) {
+  float e;
+  if constexpr (PRECISE) {
+    const double zd = z;
+    e = exp_split(-1.5957691216057307118 * (zd + 0.044715 * zd * zd * zd));
+  } else {
+    e = fast_exp(-1.5957691216057308f * fmaf(0.044715f * z, z * z, z));
+  }
+  return z * __builtin_amdgcn_rcpf(1.f + e);
+}
+
+// Activation of the epilogue. OUT: the output kind; FP32 outputs take the
+// precise GELU forms.
+template <int OUT>
 __device__ __forceinline__ float apply_act(float z, int act) {
+  constexpr bool PRECISE = OUT == OUT_F32;
   if (act == ACT_RELU) return z > 0.f ? z : 0.f;
-  if (act == ACT_GELU_ERF) {
-    const float hz = 0.5f * z;
-    return fmaf(hz, erf_as7126(z * 0.70710678118654752f), hz);
-  }
-  if (act == ACT_GELU_TANH) {
-    // tanh(u) = 1 - 2 / (1 + e^(2u)); saturates correctly for large |u|.
-    const float u = 0.79788456080286536f * (z + 0.044715f * z * z * z);  // sqrt(2/pi) (...)
-    const float th = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + fast_exp(2.f * u));
-    return 0.5f * z * (1.f + th);
-  }
+  if (act == ACT_GELU_ERF) return gelu_erf<PRECISE>(z);
+  if (act == ACT_GELU_TANH) return gelu_tanh<PRECISE>(z);
   return z;
 }
 

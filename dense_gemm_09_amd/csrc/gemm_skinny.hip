@@ -60,7 +60,7 @@ __device__ __forceinline__ void skinny_epilogue(const GemmArgs& p, const f32x4 (
       if constexpr (OUT == OUT_F32 || OUT == OUT_BF16) {
         if (p.beta != 0.f) z += p.beta * load_cin1<OUT>(p.C, off);
       }
-      z = apply_act(z + bias_v, ACT);
+      z = apply_act<OUT>(z + bias_v, ACT);
       float qs, qz;
       out_row_params<OUT>(p, m, qs, qz);
       store_out1<OUT>(p.C, off, z, qs, qz);

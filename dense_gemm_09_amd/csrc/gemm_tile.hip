@@ -495,7 +495,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
       if constexpr (SPLIT) {
         // Partials are written once and read once by the reduction: non-temporal.
         float* w = p.workspace + (static_cast<int64_t>(split) * M + m) * N + n;
-        if (vec_ok && (N & 3) == 0) {
+        // 16-byte stores where the workspace row start and this lane's
+        // column group are 16-byte aligned and the group lies inside N.
+        if (p.ws_vec && (N & 3) == 0 && n + 3 < N) {
           __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(w));
         } else {
 #pragma unroll
@@ -519,7 +521,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
             if (use_c) v[q] = fmaf(p.beta, c4[q], v[q]);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = apply_act(v[q], ACT);
+        for (int q = 0; q < 4; ++q) v[q] = apply_act<OUT>(v[q], ACT);
         const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
         if (vec_ok) {
           store_out4<OUT>(p.C, off, v, qs, qz);
@@ -1026,7 +1028,7 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs p) {
     if (p.beta != 0.f) v += p.beta * load_cin1<OUT>(p.C, off);
   }
   if (p.bias) v += bf16_bits_to_f32(p.bias[n]);
-  v = apply_act(v, p.act);
+  v = apply_act<OUT>(v, p.act);
   float qs, qz;
   out_row_params<OUT>(p, m, qs, qz);
   store_out1<OUT>(p.C, off, v, qs, qz);
@@ -1063,7 +1065,7 @@ __global__ void __launch_bounds__(256) splitk_reduce4_kernel(GemmArgs p) {
       if (p.beta != 0.f) v[q] += p.beta * load_cin1<OUT>(p.C, off + q);
     }
     if (p.bias) v[q] += bf16_bits_to_f32(p.bias[n + q]);
-    v[q] = apply_act(v[q], p.act);
+    v[q] = apply_act<OUT>(v[q], p.act);
   }
   float qs, qz;
   out_row_params<OUT>(p, m, qs, qz);
@@ -1071,32 +1073,32 @@ __global__ void __launch_bounds__(256) splitk_reduce4_kernel(GemmArgs p) {
 }
 
 // ------------------------------------------------------------------- launchers
-#ifndef G355_KERNELS_ONLY
+//
+// This file is compiled once per (ragged, output part) pair, with G355_PART
+// (an OutPart) and G355_RAGGED (0 or 1) defined, and once with G355_REDUCE
+// for the split-K reduction: each compile instantiates only the kernels of its
+// output kind, so the kernel variants build in parallel.
+#if defined(G355_PART)
 
 template <class C, int LA, int LB, bool RAGGED, bool QUANT_OUT = true>
 static hipError_t launch_cfg(const Plan& plan, const LaunchSpec& spec, const GemmArgs& a,
                              hipStream_t stream) {
+  (void)spec;
   const dim3 grid(static_cast<unsigned>(plan.grid)), block(C::NT);
-  if (plan.split > 1) {
+  constexpr int PART = G355_PART;
+  if constexpr (PART == PART_SPLIT) {
     hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_F32, true, RAGGED>), grid, block, 0,
                        stream, a);
-  } else if (spec.out == OUT_BF16) {
-    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_BF16, false, RAGGED>), grid, block, 0,
-                       stream, a);
-  } else if (spec.out == OUT_I8 || spec.out == OUT_E4M3) {
-    if constexpr (QUANT_OUT) {
-      if (spec.out == OUT_I8)
-        hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_I8, false, RAGGED>), grid, block, 0,
-                           stream, a);
-      else
-        hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_E4M3, false, RAGGED>), grid, block, 0,
-                           stream, a);
-    } else {
-      return hipErrorInvalidValue;
-    }
+  } else if constexpr (PART == PART_F32 || PART == PART_BF16) {
+    constexpr int OUT = PART == PART_F32 ? OUT_F32 : OUT_BF16;
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT, false, RAGGED>), grid, block, 0, stream,
+                       a);
+  } else if constexpr (QUANT_OUT) {
+    constexpr int OUT = PART == PART_I8 ? OUT_I8 : OUT_E4M3;
+    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT, false, RAGGED>), grid, block, 0, stream,
+                       a);
   } else {
-    hipLaunchKernelGGL((gemm_tile_kernel<C, LA, LB, OUT_F32, false, RAGGED>), grid, block, 0,
-                       stream, a);
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -1195,17 +1197,12 @@ static hipError_t launch_tile_t(const Plan& plan, const LaunchSpec& spec, const 
                   : launch_cfg<Small16, LOAD_DIRECT, LOAD_DIRECT, R>(plan, spec, a, stream);
 }
 
-#ifdef G355_TILE_RAGGED
-hipError_t launch_tile_ragged(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
-                              hipStream_t stream) {
-  return launch_tile_t<true>(plan, spec, args, stream);
+hipError_t G355_PART_LAUNCHER(G355_RAGGED, G355_PART)(const Plan& plan, const LaunchSpec& spec,
+                                                      const GemmArgs& args, hipStream_t stream) {
+  return launch_tile_t<G355_RAGGED != 0>(plan, spec, args, stream);
 }
-#else
-hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
-                       hipStream_t stream) {
-  return spec.ragged ? launch_tile_ragged(plan, spec, args, stream)
-                     : launch_tile_t<false>(plan, spec, args, stream);
-}
+
+#elif defined(G355_REDUCE)
 
 template <bool FP8, bool VEC>
 static hipError_t launch_reduce_k(const LaunchSpec& spec, const GemmArgs& a, hipStream_t stream) {
@@ -1248,7 +1245,6 @@ hipError_t launch_splitk_reduce(const Plan& plan, const LaunchSpec& spec, const 
                               : launch_reduce<false>(spec, a, stream);
 }
 
-#endif  // G355_TILE_RAGGED
-#endif  // G355_KERNELS_ONLY
+#endif  // G355_PART / G355_REDUCE
 
 }  // namespace g355

@@ -45,12 +45,25 @@ struct LaunchSpec {
   bool ragged;             // K not a multiple of the 16-byte chunk, a K-major operand DMA-fed
 };
 
-// Enqueue the kernels of a plan. Returns the HIP error of the launch(es).
+// The tile kernels are instantiated per output part, each in a compile of
+// its own (gemm_tile.hip built with G355_PART and G355_RAGGED).
+enum OutPart : int { PART_SPLIT = 0, PART_F32 = 1, PART_BF16 = 2, PART_I8 = 3, PART_E4M3 = 4 };
+constexpr int kOutParts = 5;
+
+#define G355_PART_LAUNCHER_(r, p) launch_tile_r##r##_p##p
+#define G355_PART_LAUNCHER(r, p) G355_PART_LAUNCHER_(r, p)
+#define G355_DECLARE_PART(r, p)                                                              \
+  hipError_t G355_PART_LAUNCHER(r, p)(const Plan& plan, const LaunchSpec& spec,              \
+                                      const GemmArgs& args, hipStream_t stream);
+G355_DECLARE_PART(0, 0) G355_DECLARE_PART(0, 1) G355_DECLARE_PART(0, 2) G355_DECLARE_PART(0, 3)
+G355_DECLARE_PART(0, 4) G355_DECLARE_PART(1, 0) G355_DECLARE_PART(1, 1) G355_DECLARE_PART(1, 2)
+G355_DECLARE_PART(1, 3) G355_DECLARE_PART(1, 4)
+#undef G355_DECLARE_PART
+
+// Enqueue the tile kernel of a plan (the part launcher for its output kind
+// and ragged flag). Returns the HIP error of the launch.
 hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
                        hipStream_t stream);
-// The same, for spec.ragged (instantiated in a translation unit of its own).
-hipError_t launch_tile_ragged(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
-                              hipStream_t stream);
 hipError_t launch_skinny(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
                          hipStream_t stream);
 hipError_t launch_splitk_reduce(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,

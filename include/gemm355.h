@@ -35,10 +35,15 @@
  *   K == 0 gives C = act(beta*C + bias). beta == 0 means C is not read (NaN in
  *   C is ignored).
  * - Errors: every argument check happens before anything is enqueued; on a
- *   non-OK status nothing was launched and no memory was touched. After the
- *   launch, a HIP launch error is reported as GEMM_ERR_HIP. Faults inside a
- *   kernel surface at the caller's next synchronisation. Nothing is printed
- *   and nothing aborts.
+ *   status other than GEMM_OK and GEMM_ERR_HIP nothing was launched and no
+ *   memory was touched. GEMM_ERR_HIP means the HIP runtime rejected one of the
+ *   call's launches; a call of two launches (a split-K GEMM and its
+ *   reduction) whose second launch fails has already enqueued the first, which
+ *   writes only the workspace. Before launching, the call consumes any HIP
+ *   error that an earlier call on the same thread left pending (hipGetLastError),
+ *   so GEMM_ERR_HIP never reports someone else's error. Faults inside a kernel
+ *   surface at the caller's next synchronisation. Nothing is printed and
+ *   nothing aborts.
  * - Aliasing: C must not overlap A, B, bias, the scales or the workspace.
  * - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null
  *   stream) and the call returns without waiting.

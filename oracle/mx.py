@@ -10,7 +10,7 @@ of A and each column of B:
 
     a'(m, k) = e4m3(A[m, k]) * 2^(SA[m, k // 32] - 127)
     b'(k, n) = e4m3(B[n, k]) * 2^(SB[n, k // 32] - 127)
-    acc      = sum_k a'(m, k) b'(k, n)                (float64)
+    acc      = sum_k a'(m, k) b'(k, n)     (float64, ascending k: the triple loop)
     then the same epilogue as the other GEMMs (alpha, beta * C_in, bias, act, cast)
 
 A is row-major (K-major), B column-major (K-major): the layouts of the page's
@@ -28,7 +28,7 @@ from __future__ import annotations
 import numpy as np
 
 from .codecs import decode_e4m3
-from .gemm import ROW, COL, _epilogue, _select, logical_a, logical_b
+from .gemm import ROW, COL, _epilogue, _product, _select, logical_a, logical_b
 
 MX_BLOCK = 32
 
@@ -47,18 +47,18 @@ def _block_scales(S: np.ndarray, rows, K: int) -> np.ndarray:
 
 
 def gemm_mxfp8(M, N, K, alpha, A, B, scale_a, scale_b, beta, C, c_dtype, bias, act,
-               rows=None, cols=None):
+               rows=None, cols=None, with_z=False):
     """MX FP8 GEMM. A: E4M3 codes (M x lda), B: E4M3 codes (N x ldb, K-major),
-    scale_a: E8M0 codes (M x ldsa), scale_b: (N x ldsb). Returns (y, out)."""
+    scale_a: E8M0 codes (M x ldsa), scale_b: (N x ldsb). Returns (y, out), or
+    (y, out, z) with with_z."""
     r, c = _select(M, N, rows, cols)
     a = decode_e4m3(logical_a(A, ROW, M, K)[r, :])
     b = decode_e4m3(logical_b(B, COL, K, N)[:, c])
     if K > 0:
         a = a * _block_scales(scale_a, r, K)
         b = b * _block_scales(scale_b, c, K).T
-        acc = a @ b
-    else:
-        acc = np.zeros((len(r), len(c)))
+    acc = _product(a, b)
     C_sel = C[np.ix_(r, c)] if beta != 0.0 else None
     bias_sel = None if bias is None else np.asarray(bias)[c]
-    return _epilogue(acc, alpha, beta, C_sel, c_dtype, bias_sel, act)
+    res = _epilogue(acc, alpha, beta, C_sel, c_dtype, bias_sel, act)
+    return res if with_z else res[:2]

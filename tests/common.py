@@ -7,17 +7,19 @@ import oracle
 from tests import tolerance
 
 
-def reference(p, rows=None, cols=None):
-    """(y, out) from the oracle for problem p, optionally on a row/column sample."""
+def reference(p, rows=None, cols=None, with_z=False):
+    """(y, out) from the oracle for problem p, optionally on a row/column sample;
+    (y, out, z) with with_z (z: the pre-activation values)."""
     if p.kind == "bf16":
         return oracle.gemm_bf16(p.M, p.N, p.K, p.alpha, p.A, p.layout_a, p.B, p.layout_b,
-                                p.beta, p.C, p.c_dtype, p.bias, p.act, rows=rows, cols=cols)
+                                p.beta, p.C, p.c_dtype, p.bias, p.act, rows=rows, cols=cols,
+                                with_z=with_z)
     if p.kind == "mxfp8":
         return oracle.gemm_mxfp8(p.M, p.N, p.K, p.alpha, p.A, p.B, p.mx_a, p.mx_b, p.beta, p.C,
-                                 p.c_dtype, p.bias, p.act, rows=rows, cols=cols)
+                                 p.c_dtype, p.bias, p.act, rows=rows, cols=cols, with_z=with_z)
     return oracle.gemm_fp8_scaled(p.M, p.N, p.K, p.alpha, p.A, p.layout_a, p.B, p.layout_b,
                                   p.scale_a, p.scale_b, p.beta, p.C, p.c_dtype, p.bias, p.act,
-                                  rows=rows, cols=cols)
+                                  rows=rows, cols=cols, with_z=with_z)
 
 
 def operand_norms(p, rows=None, cols=None):
@@ -41,11 +43,14 @@ def operand_norms(p, rows=None, cols=None):
 
 def compare(p, out, rows=None, cols=None, what=""):
     """Check a result (M'xN' array: float32, or uint16 BF16 codes) against the oracle."""
-    y, ref = reference(p, rows, cols)
+    y, ref, z = reference(p, rows, cols, with_z=True)
     rn, cn = operand_norms(p, rows, cols)
     what = what or p.name
     if p.c_dtype == 0:
-        return tolerance.check_f32(out, y, rn, cn, p.alpha, what,
-                                   frob=1e-5 if p.kind == "bf16" else 1e-4)
-    return tolerance.check_bf16(oracle.decode_bf16(out), y, oracle.decode_bf16(ref), rn, cn,
-                                p.alpha, p.act, what)
+        info = tolerance.check_f32(out, y, rn, cn, p.alpha, what,
+                                   frob=1e-5 if p.kind == "bf16" else 1e-4, z=z, act=p.act)
+    else:
+        info = tolerance.check_bf16(oracle.decode_bf16(out), y, oracle.decode_bf16(ref), rn, cn,
+                                    p.alpha, p.act, what, z=z)
+    print(f"[parity] {what}: {info}", flush=True)
+    return info

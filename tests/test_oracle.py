@@ -8,10 +8,17 @@
   the drawn integers), tiny operands with hand-chosen dyadic values (checked
   against rational arithmetic), identity and permutation matrices, closed
   forms for the scales and the bias, alpha/beta linearity;
+* the epilogue's order in closed form: alpha scales the product only (not
+  beta*C_in, not the bias), and the activation sees beta*C_in and the bias
+  (first DeepGEMM page, sec. 1.1 and 6.1);
+* the accumulation order: ascending k in float64, shown by a sum whose float64
+  value depends on the order;
 * GELU against tabulated values of the standard normal CDF;
 * a planted-mistake check: oracles with a dropped term, a transposed
-  operand or a wrong sign fail the parity tolerance.
+  operand, a wrong sign, a misplaced alpha or an activation applied too early
+  fail the parity tolerance.
 """
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -228,6 +235,59 @@ def test_alpha_linearity_and_beta_cancellation():
     assert np.array_equal(out5, 4 * out1)
 
 
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_alpha_scales_product_only(kind):
+    """alpha = 2, beta = 3, C_in = A B, integer bias b: out = 2 AB + 3 AB + b = 5 AB + b
+    exactly. A reading where alpha also scaled beta*C_in (8 AB + b) or the bias
+    (5 AB + 2b) gives another integer."""
+    M, N, K = 12, 10, 24
+    base = 0x6262000
+    lo, hi = (-4, 4) if kind == "bf16" else (-16, 16)
+    p = synth.make_problem(kind, M, N, K, seed_base=base, int_range=(lo, hi), c_dtype=OUT_F32)
+    ab = (synth.small_ints((M, K), lo, hi, base).astype(np.int64)
+          @ synth.small_ints((K, N), lo, hi, base + 1).astype(np.int64))
+    bias_vals = np.arange(N, dtype=np.float64) * 3 - 13   # nonzero integers, exact in BF16
+    p.bias = synth.to_bf16_bits(bias_vals)
+    p.alpha, p.beta = 2.0, 3.0
+    p.C = ab.astype(np.float32)
+    _, out = reference(p)
+    assert np.array_equal(out, (5 * ab + bias_vals[None, :]).astype(np.float32))
+
+
+@pytest.mark.parametrize("act", [ACT_RELU, ACT_GELU_ERF])
+def test_activation_sees_beta_c_and_bias(act):
+    """A = 1, so A B has equal rows s_n = sum_k B[k, n] (integers). With
+    beta*C_in = -s_n - 1 and bias +0.5 every z is exactly -0.5: ReLU gives 0 and
+    GELU gives -0.5 Phi(-0.5) (normal-CDF table). Applying the activation before
+    adding beta*C_in or the bias would give act(s_n) - s_n - 1 (+0.5) instead."""
+    M, N, K = 6, 9, 16
+    base = 0x6363000
+    b = synth.small_ints((K, N), -4, 4, base + 1).astype(np.int64)
+    s_n = b.sum(axis=0)
+    A = synth.to_bf16_bits(np.ones((M, K)))
+    B = synth.to_bf16_bits(b.astype(np.float64))
+    C = np.tile((-s_n - 1).astype(np.float32), (M, 1))
+    bias = synth.to_bf16_bits(np.full(N, 0.5))
+    y, out = oracle.gemm_bf16(M, N, K, 1.0, A, ROW, B, ROW, 1.0, C, OUT_F32, bias, act)
+    expect = 0.0 if act == ACT_RELU else -0.5 * (1.0 - PHI[0.5])
+    assert np.all(np.abs(y - expect) <= 1e-15), (y, expect)
+    assert np.any(s_n != -1)  # the mutant readings differ somewhere
+
+
+def test_accumulation_is_ascending_k_in_float64():
+    """Products 2^53, 1, -2^53 in this k order: (2^53 + 1) rounds to 2^53 in
+    float64 (tie to even), so the ascending-k float64 sum is 0; in the reverse
+    order it is (-2^53 + 1) + 2^53 = 1. Both are exact FP32 outputs."""
+    A = synth.to_bf16_bits(np.array([[2.0 ** 26, 1.0, -(2.0 ** 26)]]))
+    B = synth.to_bf16_bits(np.array([[2.0 ** 27], [1.0], [2.0 ** 27]]))
+    C = np.zeros((1, 1), np.float32)
+    _, out = oracle.gemm_bf16(1, 1, 3, 1.0, A, ROW, B, ROW, 0.0, C, OUT_F32, None, ACT_NONE)
+    assert out[0, 0] == 0.0
+    _, out = oracle.gemm_bf16(1, 1, 3, 1.0, A[:, ::-1].copy(), ROW, B[::-1].copy(), ROW, 0.0, C,
+                              OUT_F32, None, ACT_NONE)
+    assert out[0, 0] == 1.0
+
+
 def test_beta_zero_does_not_read_c():
     p = synth.make_problem("bf16", 8, 8, 8, seed_base=0x7171000)
     p.C[:] = np.nan
@@ -273,6 +333,48 @@ def test_gelu_erf_against_normal_cdf_table():
     assert float(oracle.activation(np.float64(0.0), ACT_GELU_ERF)) == 0.0
 
 
+def _normal_tail(x: float) -> float:
+    """1 - Phi(x) for large x from the asymptotic series of Mills' ratio,
+    phi(x)/x * sum_n (-1)^n (2n-1)!! / x^(2n) (alternating: the error is below
+    the first omitted term)."""
+    total, term = 0.0, 1.0
+    for n in range(1, 12):
+        total += term
+        term *= -(2 * n - 1) / (x * x)
+    return math.exp(-0.5 * x * x) / math.sqrt(2 * math.pi) / x * total
+
+
+@pytest.mark.parametrize("x", [9.0, 10.0, 12.0, 20.0])
+def test_gelu_erf_far_negative_tail(x):
+    """GELU(-x) = -x (1 - Phi(x)): relative accuracy where Phi is tiny (the
+    series' truncation error at these x is below 1e-11 relative)."""
+    got = float(oracle.activation(np.float64(-x), ACT_GELU_ERF))
+    want = -x * _normal_tail(x)
+    assert want < 0 and abs(got - want) <= 1e-10 * abs(want), (x, got, want)
+
+
+def _gelu_tanh_decimal(z: float) -> float:
+    """0.5 z (1 + tanh u), u = sqrt(2/pi) (z + 0.044715 z^3), in 300-digit decimal
+    arithmetic with tanh u = (e^(2u) - 1) / (e^(2u) + 1): the definition itself,
+    evaluated far beyond float64 precision."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 300
+    zd = Decimal(z)
+    pi = Decimal("3.14159265358979323846264338327950288419716939937510582097494459")
+    u = (Decimal(2) / pi).sqrt() * (zd + Decimal("0.044715") * zd ** 3)
+    e2u = (2 * u).exp()
+    return float(Decimal("0.5") * zd * (1 + (e2u - 1) / (e2u + 1)))
+
+
+@pytest.mark.parametrize("z", [-15.0, -12.0, -9.0, -5.0, -1.0, -0.25, 0.5, 3.0, 8.0])
+def test_gelu_tanh_against_high_precision_definition(z):
+    got = float(oracle.activation(np.float64(z), ACT_GELU_TANH))
+    want = _gelu_tanh_decimal(z)
+    # float64 rounding of u alone moves e^(2u) by ~|2u| * 2^-52 relative
+    u = math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3)
+    assert abs(got - want) <= (1e-15 + 8 * abs(2 * u) * 2.0 ** -53) * abs(want), (z, got, want)
+
+
 def test_gelu_tanh_properties():
     x = np.linspace(-8, 8, 20001)
     g = oracle.activation(x, ACT_GELU_TANH)
@@ -297,6 +399,21 @@ def test_sampled_rows_match_full():
 def _mutant(p, how):
     """The oracle with a planted mistake (CPU only)."""
     q = synth.Problem(**{f: getattr(p, f) for f in p.__dataclass_fields__})
+    if how in ("alpha_scales_bias", "alpha_scales_beta_c", "act_before_beta_c", "act_before_bias"):
+        # the product alone (alpha 1, no C_in, no bias, no activation), then
+        # the epilogue terms combined in a wrong order
+        acc, _ = reference(synth.Problem(**{**q.__dict__, "alpha": 1.0, "beta": 0.0, "bias": None,
+                                            "act": ACT_NONE}))
+        bc = p.beta * p.C.astype(np.float64)
+        b = oracle.decode_bf16(p.bias)[None, :]
+        act = lambda z: oracle.activation(z, p.act)
+        if how == "alpha_scales_bias":
+            return act(p.alpha * (acc + b) + bc)
+        if how == "alpha_scales_beta_c":
+            return act(p.alpha * (acc + bc) + b)
+        if how == "act_before_beta_c":
+            return act(p.alpha * acc + b) + bc
+        return act(p.alpha * acc + bc) + b
     if how == "drop_last_k":
         y, _ = reference(synth.Problem(**{**q.__dict__, "K": p.K - 1}))
     elif how == "transpose_b":
@@ -313,18 +430,52 @@ def _mutant(p, how):
     return y
 
 
-@pytest.mark.parametrize("how", ["drop_last_k", "transpose_b", "beta_sign", "bias_off_by_one"])
-def test_tolerance_rejects_planted_mistakes(how):
+@pytest.mark.parametrize("how", ["drop_last_k", "transpose_b", "beta_sign", "bias_off_by_one",
+                                 "alpha_scales_bias", "alpha_scales_beta_c", "act_before_beta_c",
+                                 "act_before_bias"])
+@pytest.mark.parametrize("act", [ACT_RELU, ACT_GELU_ERF])
+def test_tolerance_rejects_planted_mistakes(how, act):
     n = 64
-    p = synth.make_problem("bf16", n, n, n, seed_base=0x9191000, beta=0.5, bias_std=0.1,
-                           layout_b=COL, c_dtype=OUT_F32)
-    y_true, _ = reference(p)
+    p = synth.make_problem("bf16", n, n, n, seed_base=0x9191000, alpha=1.5, beta=0.5,
+                           bias_std=0.5, act=act, layout_b=COL, c_dtype=OUT_F32)
+    y_true, _, z = reference(p, with_z=True)
     y_bad = _mutant(p, how)
     rn, cn = operand_norms(p)
     with pytest.raises(AssertionError):
-        tolerance.check_f32(y_bad.astype(np.float32), y_true, rn, cn)
-    # and the true oracle's own float32 output passes
-    tolerance.check_f32(y_true.astype(np.float32), y_true, rn, cn)
+        tolerance.check_f32(y_bad.astype(np.float32), y_true, rn, cn, p.alpha, z=z, act=act)
+    with pytest.raises(AssertionError):
+        tolerance.check_bf16(oracle.decode_bf16(oracle.round_to_bf16_bits(y_bad)), y_true,
+                             oracle.round_to_bf16(y_true), rn, cn, p.alpha, act, z=z)
+    # and the true oracle's own outputs pass
+    tolerance.check_f32(y_true.astype(np.float32), y_true, rn, cn, p.alpha, z=z, act=act)
+    tolerance.check_bf16(oracle.round_to_bf16(y_true), y_true, oracle.round_to_bf16(y_true), rn,
+                         cn, p.alpha, act, z=z)
+
+
+def test_slope_bound_against_sampling():
+    """slope_bound(z, e) is the largest |GELU'| on [z - e, z + e]: compare with a
+    dense sample of each interval (and the tanh form's margin above it)."""
+    rng = np.random.default_rng(11)
+    z = rng.uniform(-12, 12, 400)
+    e = rng.uniform(0, 3, 400)
+    L = tolerance.slope_bound(z, e, ACT_GELU_ERF)
+    for zi, ei, Li in zip(z, e, L):
+        t = np.linspace(zi - ei, zi + ei, 2001)
+        sampled = np.abs(tolerance.gelu_slope(t)).max()
+        assert sampled <= Li + 1e-12 and Li <= sampled + 1e-3, (zi, ei, Li, sampled)
+    assert np.all(tolerance.slope_bound(z, e, ACT_RELU) == (z + e > 0))
+    # far into the negative range the slope, and so the allowance, is tiny
+    assert tolerance.slope_bound(np.float64(-8.0), 0.01, ACT_GELU_ERF) < 1e-12
+
+
+def test_tanh_gelu_slope_margin():
+    """|d/dz tanh-GELU - d/dz erf-GELU| < TANH_SLOPE_MARGIN everywhere (the
+    tanh form's slope bound is the erf form's plus that margin)."""
+    z = np.linspace(-12, 12, 240001)
+    h = 1e-5
+    d_tanh = (oracle.activation(z + h, ACT_GELU_TANH) - oracle.activation(z - h, ACT_GELU_TANH)) / (2 * h)
+    d_erf = tolerance.gelu_slope(z)
+    assert np.max(np.abs(d_tanh - d_erf)) < tolerance.TANH_SLOPE_MARGIN
 
 
 def test_bf16_tolerance_rejects_two_ulp_error():

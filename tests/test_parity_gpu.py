@@ -302,3 +302,25 @@ def test_graph_replay_matches_eager(kind, M, N, K):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(d["C"], eager)
+
+
+def test_split_k_on_side_stream_binding_workspace():
+    """With no workspace argument the binding allocates the split-K workspace on
+    the stream the call runs on, so allocations made right after the call on
+    the current stream cannot be handed the workspace's memory while the side
+    stream's kernels still use it."""
+    import torch
+    M, N, K = 64, 4096, 4096
+    pl = g.plan(M, N, K, False)
+    assert pl.split_k > 1 and pl.workspace_bytes > 0
+    p = synth.make_problem("bf16", M, N, K, seed_base=0xC10000, c_dtype=OUT_BF16, a_std=1.0,
+                           b_std=0.02)
+    d = to_device(p)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    print(f"[gpu] side-stream split-K M={M} N={N} K={K} split={pl.split_k}", flush=True)
+    call(p, d, stream=side)
+    junk = [torch.full((pl.workspace_bytes // 4,), float("nan"), device="cuda") for _ in range(4)]
+    torch.cuda.synchronize()
+    del junk
+    compare(p, d["C"].cpu().numpy().view(np.uint16)[:, :N])

@@ -8,8 +8,9 @@ the 256- and 128-wide tiles with ragged edges, split-K with its reduction
 kernel, the skinny decode kernel, and the register loader (row-major B).
 
 Random cases: the kernel's FP32 y differs from the oracle's by at most the
-parity bound of the FP32 path (1e-4 |alpha| ||a_m|| ||b_n||, x 1.13 under
-GELU, plus a few FP32 ulps and the erf approximation), so each code must lie
+parity bound of the FP32 path (1e-4 |alpha| ||a_m|| ||b_n||, times the
+activation's largest slope near z, plus a few FP32 ulps and the activation's
+FP32 evaluation error; tests/tolerance.py), so each code must lie
 between the oracle's codes for y - e and y + e (the quantiser is monotone for
 positive scales). That bound is conservative (Cauchy-Schwarz on the worst
 case); the actual error of a BF16 GEMM is near 1e-6 relative, so the test
@@ -30,6 +31,7 @@ import oracle
 from oracle import QOUT_E4M3, QOUT_INT8
 from synth import ACT_GELU_ERF, ACT_NONE, ACT_RELU, COL, ROW, make_problem
 from tests.common import operand_norms, reference
+from tests import tolerance
 from tests.tolerance import ulp_f32
 
 pytestmark = pytest.mark.gpu
@@ -135,11 +137,10 @@ def test_exact_codes(case, q_dtype):
 def bracket_check(p, q_u8, s, zp, q_dtype, rows=None, cols=None, min_exact=None):
     if min_exact is None:
         min_exact = 0.999 if p.kind == "bf16" else 0.98
-    y, _ = reference(p, rows, cols)
+    y, _, z = reference(p, rows, cols, with_z=True)
     rn, cn = operand_norms(p, rows, cols)
     e = 1e-4 * abs(p.alpha) * np.outer(rn, cn)
-    if p.act in (2, 3):
-        e = e * 1.13 + 1e-6 * np.abs(y) + 1e-7
+    e = e * tolerance.slope_bound(z, e, p.act) + tolerance.ACT_REL[p.act] * np.abs(y)
     e = e + 4 * ulp_f32(y)
     r = np.arange(p.M) if rows is None else np.asarray(rows)
     s_sel = np.asarray(s)[r]
