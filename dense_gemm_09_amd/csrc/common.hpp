@@ -151,29 +151,12 @@ __device__ __forceinline__ float load_cin1(const void* C, int64_t off) {
 
 // ---------------------------------------------------------------- epilogue math
 
-// e^x from the hardware base-2 exponential (v_exp_f32).
-__device__ __forceinline__ float fast_exp(float x) {
-  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
-}
-
-// e^a for a double a, to about one FP32 ulp for any a: a*log2(e) = n + f with
-// n integral and |f| <= 1/2 (both exact in double), 2^f from the hardware
-// exponential, 2^n applied exactly by ldexp. fast_exp loses relative accuracy
-// for large |x| instead (x*log2(e) is rounded to FP32, an absolute error of up
-// to ~4e-6 in the exponent near the FP32 underflow).
-__device__ __forceinline__ float exp_split(double a) {
-  double q = a * 1.4426950408889634074;
-  q = q < -400.0 ? -400.0 : (q > 400.0 ? 400.0 : q);  // past FP32's range either way
-  const double n = __builtin_rint(q);
-  const float r = __builtin_amdgcn_exp2f(static_cast<float>(q - n));
-  return __builtin_ldexpf(r, static_cast<int>(n));
-}
-
 // P(t) of the Chebyshev-fitted complementary error function of Numerical
 // Recipes in C (2nd ed., sec. 6.2, "erfcc"): for x >= 0,
 //   erfc(x) = t exp(-x^2 + P(t)),  t = 1 / (1 + x/2),
 // with a fractional error below 1.2e-7 for every x. Unlike 1 - erf(x), it
-// keeps its relative accuracy where erfc(x) is tiny.
+// keeps its relative accuracy where erfc(x) is tiny. P(1) = 0 (erfc(0) = 1)
+// and P(t) <= 0 on (0, 1].
 __device__ __forceinline__ float erfc_cheb_poly(float t) {
   float p = 0.17087277f;
   p = fmaf(p, t, -0.82215223f);
@@ -188,43 +171,70 @@ __device__ __forceinline__ float erfc_cheb_poly(float t) {
   return p;
 }
 
-// GELU(z) = z Phi(z), Phi(z) = erfc(-z / sqrt 2) / 2: Phi(z) = e/2 for z < 0
-// and 1 - e/2 for z >= 0 with e = erfc(|z| / sqrt 2), so the result keeps its
-// relative accuracy on both sides (far into the negative range it is a tiny
-// number, not the difference of two numbers near 1). The exponent -z^2/2 + P
-// is one fused multiply-add from z itself (0.5 z is exact). PRECISE forms it
-// in double and takes e^a by exp_split: relative error ~1e-6 for every z
-// (FP32 outputs); otherwise the FP32 exponent's rounding leaves a relative
-// error of up to ~1e-5 at the far negative end, far below a BF16 ulp.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kTwoM64 = 5.42101086242752217e-20f;  // 2^-64
+
+// 2^q for a double q <= 0 as (r, n) with 2^q = r * 2^n, n integral, r in
+// [2^-0.5, 2^0.5] from the hardware exponential: the FP32 rounding sees only
+// the fraction, so r carries about one FP32 ulp of error whatever q is.
+__device__ __forceinline__ float exp2_split(double q, int& n) {
+  q = q < -400.0 ? -400.0 : q;  // far past FP32's range either way
+  const double nd = __builtin_rint(q);
+  n = static_cast<int>(nd);
+  return __builtin_amdgcn_exp2f(static_cast<float>(q - nd));
+}
+
+// GELU(z) = z Phi(z) = z - w for z >= 0 and w for z < 0, where
+//   w = (z/2) erfc(|z|/sqrt 2) = (z/2) t exp(P(t) - z^2/2)
+// (Phi(z) = erfc(-z/sqrt 2)/2). No difference of nearby numbers is formed, so
+// the result keeps its relative accuracy far into the negative range, and the
+// exponential's power-of-two scale is applied last, so that w stays accurate
+// down into FP32's subnormal range (erfc alone, smaller by |z|/2, would
+// underflow first). The exponent P - z^2/2 is one fused multiply-add from z
+// itself (z/2 is exact). PRECISE forms it in double and splits off its power
+// of two exactly (relative error ~5e-7 for every z; FP32 outputs); otherwise
+// it is scaled by 2^64 inside the exponential and 2^-64 at the end, and its
+// FP32 rounding leaves a relative error of up to ~1e-5 at the far negative
+// end, far below a BF16 ulp.
 template <bool PRECISE>
 __device__ __forceinline__ float gelu_erf(float z) {
+  const float hz = 0.5f * z;
   const float x = fabsf(z) * 0.70710678118654752f;
   const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, x, 1.f));
   const float p = erfc_cheb_poly(t);
-  float e;
+  float w;
   if constexpr (PRECISE) {
     const double zd = z;
-    e = t * exp_split(static_cast<double>(p) - 0.5 * zd * zd);
+    int n;
+    const float r = exp2_split((static_cast<double>(p) - 0.5 * zd * zd) * 1.4426950408889634074, n);
+    w = __builtin_ldexpf(hz * t * r, n);
   } else {
-    e = t * fast_exp(fmaf(-0.5f * z, z, p));
+    const float r = __builtin_amdgcn_exp2f(fmaf(fmaf(-hz, z, p), kLog2e, 64.f));
+    w = (hz * t * r) * kTwoM64;
   }
-  const float phi = z < 0.f ? 0.5f * e : fmaf(-0.5f, e, 1.f);
-  return z * phi;
+  return z < 0.f ? w : z - w;
 }
 
-// tanh-form GELU: 0.5 z (1 + tanh u) = z / (1 + e^(-2u)), u = sqrt(2/pi)
-// (z + 0.044715 z^3); no cancellation for either sign of z. PRECISE forms u
-// and e^(-2u) in double / by exp_split.
+// tanh-form GELU: 0.5 z (1 + tanh u) = z / (1 + e^(-a)), a = 2u = 2 sqrt(2/pi)
+// (z + 0.044715 z^3). With E = e^(-|a|) in (0, 1]: z / (1 + E) for z >= 0, and
+// z E / (1 + E) for z < 0 (no cancellation for either sign), E's power-of-two
+// scale applied last as in gelu_erf. PRECISE forms a and E in double /
+// by exp2_split.
 template <bool PRECISE>
 __device__ __forceinline__ float gelu_tanh(float z) {
-  float e;
   if constexpr (PRECISE) {
     const double zd = z;
-    e = exp_split(-1.5957691216057307118 * (zd + 0.044715 * zd * zd * zd));
+    const double a = 1.5957691216057307118 * (zd + 0.044715 * zd * zd * zd);
+    int n;
+    const float r = exp2_split(-__builtin_fabs(a) * 1.4426950408889634074, n);
+    const float d = __builtin_amdgcn_rcpf(1.f + __builtin_ldexpf(r, n));
+    return z < 0.f ? __builtin_ldexpf(z * r * d, n) : z * d;
   } else {
-    e = fast_exp(-1.5957691216057308f * fmaf(0.044715f * z, z * z, z));
+    const float s = fmaf(0.044715f * z, z * z, z);  // u / sqrt(2/pi)
+    const float r = __builtin_amdgcn_exp2f(fmaf(-fabsf(s), 1.5957691216057308f * kLog2e, 64.f));
+    const float d = __builtin_amdgcn_rcpf(fmaf(r, kTwoM64, 1.f));
+    return z < 0.f ? (z * r * d) * kTwoM64 : z * d;
   }
-  return z * __builtin_amdgcn_rcpf(1.f + e);
 }
 
 // Activation of the epilogue. OUT: the output kind; FP32 outputs take the
