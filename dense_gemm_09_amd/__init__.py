@@ -26,7 +26,7 @@ ACT_NONE, ACT_RELU, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2, 3
 STATUS = ["GEMM_OK", "GEMM_ERR_NULL_POINTER", "GEMM_ERR_BAD_DIM", "GEMM_ERR_BAD_LD",
           "GEMM_ERR_BAD_ENUM", "GEMM_ERR_UNSUPPORTED", "GEMM_ERR_WORKSPACE_TOO_SMALL",
           "GEMM_ERR_HIP"]
-EXPORTS = ["gemm_bf16", "gemm_fp8_scaled", "gemm_mxfp8", "gemm_bf16_quant", "gemm_fp8_scaled_quant",
+EXPORTS = ["gemm_bf16", "gemm_bf16_noalloc", "gemm_fp8_scaled", "gemm_mxfp8", "gemm_bf16_quant", "gemm_fp8_scaled_quant",
            "gemm_quantize_fp8_rows", "gemm_pack_b", "gemm_workspace_size", "gemm_plan",
            "gemm_status_string"]
 
@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.gemm_bf16.restype = _I32
         L.gemm_bf16.argtypes = [_I64, _I64, _I64, _F32, _P, _I64, _I32, _P, _I64, _I32, _F32,
                                 _P, _I64, _I32, _P, _I32, _P, _SZ, _P]
+        L.gemm_bf16_noalloc.restype = _I32
+        L.gemm_bf16_noalloc.argtypes = [_I64, _I64, _I64, _F32, _P, _I64, _I32, _P, _I64, _I32,
+                                        _F32, _P, _I64, _I32, _P, _I32, _P]
         L.gemm_fp8_scaled.restype = _I32
         L.gemm_fp8_scaled.argtypes = [_I64, _I64, _I64, _F32, _P, _I64, _I32, _P, _I64, _I32,
                                       _P, _P, _F32, _P, _I64, _I32, _P, _I32, _P, _SZ, _P]
@@ -165,6 +168,18 @@ def gemm_bf16(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, beta, C, ldc, 
                      _stream(stream))
     if st != 0:
         raise GemmError(st, "gemm_bf16")
+
+
+def gemm_bf16_noalloc(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, beta, C, ldc, c_dtype,
+                      bias=None, act=ACT_NONE, stream=None):
+    """gemm_bf16 without a workspace: split-K partials go to the library's
+    per-GPU scratch array (nothing is allocated; calls overlapping on one GPU race)."""
+    L = lib()
+    _check_operands(M, N, K, A, lda, layout_a, B, ldb, layout_b, C, ldc, c_dtype, 2, bias)
+    st = L.gemm_bf16_noalloc(M, N, K, alpha, _ptr(A), lda, layout_a, _ptr(B), ldb, layout_b,
+                             beta, _ptr(C), ldc, c_dtype, _ptr(bias), act, _stream(stream))
+    if st != 0:
+        raise GemmError(st, "gemm_bf16_noalloc")
 
 
 def gemm_fp8_scaled(M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, scale_a, scale_b,

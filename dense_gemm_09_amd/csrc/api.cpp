@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "gemm355.h"
 #include "internal.hpp"
@@ -343,6 +344,37 @@ gemm_status run(bool fp8, int64_t M, int64_t N, int64_t K, float alpha, const vo
   return GEMM_OK;
 }
 
+// ---- scratch of the entry point that allocates nothing (gemm_bf16_noalloc)
+//
+// A file-scope device array: every GPU the library runs on holds one copy of
+// it from the module load until the process ends. In host code the name
+// `scratch` is only a host-side stand-in for the array, not a device
+// address, so it is never passed to a kernel or a copy: the device address of
+// each GPU's copy is taken once per device with hipGetSymbolAddress (with
+// that device current) and kept in g_scratch_ptr.
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call on that
+// device).
+gemm_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GEMM_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return GEMM_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -354,6 +386,29 @@ gemm_status gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const void* 
   if (!valid_out(c_dtype)) return GEMM_ERR_BAD_ENUM;
   return run(false, M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, nullptr, nullptr, beta,
              C, ldc, c_dtype, nullptr, nullptr, bias, act, workspace, workspace_bytes, stream);
+}
+
+gemm_status gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, float alpha, const void* A,
+                              int64_t lda, gemm_layout layout_a, const void* B, int64_t ldb,
+                              gemm_layout layout_b, float beta, void* C, int64_t ldc,
+                              gemm_out_dtype c_dtype, const void* bias, gemm_act act,
+                              void* stream) {
+  if (!valid_out(c_dtype)) return GEMM_ERR_BAD_ENUM;
+  // The split-K partials go to this device's scratch array: no allocation.
+  // The partials are written in full before they are read (nothing needs to
+  // start at zero); calls that overlap on one GPU share the array and race.
+  size_t need = 0;
+  if (M > 0 && N > 0 && K >= 0 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim)
+    need = make_plan(M, N, K, false).workspace;
+  if (need > kNoAllocScratchBytes) return GEMM_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (need > 0) {
+    const gemm_status st = scratch_of_current_device(&ws);
+    if (st != GEMM_OK) return st;
+  }
+  return run(false, M, N, K, alpha, A, lda, layout_a, B, ldb, layout_b, nullptr, nullptr, beta,
+             C, ldc, c_dtype, nullptr, nullptr, bias, act, ws, ws ? kNoAllocScratchBytes : 0,
+             stream);
 }
 
 gemm_status gemm_fp8_scaled(int64_t M, int64_t N, int64_t K, float alpha, const void* A,

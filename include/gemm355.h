@@ -96,6 +96,28 @@ gemm_status gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gemm_bf16 for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same operation, arguments and kernels, without a workspace argument. Split-K
+ * partials go to a scratch array of 32 MiB that the library holds in every
+ * GPU's memory from the module load until the process ends; the call
+ * allocates and frees nothing. A shape whose plan needs more workspace than
+ * that returns GEMM_ERR_WORKSPACE_TOO_SMALL (gemm_workspace_size(M, N, K, 0)
+ * tells in advance) before anything is launched. The scratch of the calling
+ * thread's current device is used, so that device must be the one the
+ * stream and pointers belong to. All calls on one GPU share its array: calls
+ * that overlap in time (on different streams, or from several threads) race
+ * and give undefined results; calls ordered on one stream are safe. The first
+ * call on each device looks up the array's device address
+ * (hipGetSymbolAddress); a failure there returns GEMM_ERR_HIP.
+ */
+gemm_status gemm_bf16_noalloc(int64_t M, int64_t N, int64_t K, float alpha,
+                              const void* A, int64_t lda, gemm_layout layout_a,
+                              const void* B, int64_t ldb, gemm_layout layout_b,
+                              float beta, void* C, int64_t ldc, gemm_out_dtype c_dtype,
+                              const void* bias, gemm_act act, void* stream);
+
+/*
  * OCP FP8 E4M3 x E4M3 -> FP32 accumulate -> x scale_a[m]*scale_b[n] -> epilogue.
  * A must be ROW (K-major, per-token rows) and B COL (K-major, per-channel
  * rows); other layouts return GEMM_ERR_UNSUPPORTED. scale_a (FP32[M]) and

@@ -1,0 +1,76 @@
+"""gemm_bf16_noalloc, the entry point that allocates nothing, against gemm_bf16.
+
+Both calls run the same plan and kernels; gemm_bf16_noalloc only takes its
+split-K partials from the library's per-GPU scratch array instead of a caller
+workspace. So its output must equal gemm_bf16's bit for bit (and both pass the
+oracle's tolerance). Two calls in a row, the second smaller than the first,
+show that the scratch array's contents from one call do not leak into the
+next; a shape whose workspace exceeds the array is refused before anything is
+launched.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import dense_gemm_09_amd as g
+import synth
+from synth import ACT_GELU_ERF, OUT_BF16, OUT_F32
+from tests.common import compare
+from tests.gpu_util import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(p):
+    import torch
+    pl = g.plan(p.M, p.N, p.K, False)
+    print(f"[gpu] noalloc vs gemm_bf16 M={p.M} N={p.N} K={p.K} split={pl.split_k} "
+          f"workspace={pl.workspace_bytes}", flush=True)
+    d = to_device(p)
+    c_ref = d["C"].clone()
+    ws = torch.empty(max(1, pl.workspace_bytes), dtype=torch.uint8, device="cuda")
+    g.gemm_bf16(p.M, p.N, p.K, p.alpha, d["A"], p.lda, p.layout_a, d["B"], p.ldb, p.layout_b,
+                p.beta, c_ref, p.ldc, p.c_dtype, d["bias"], p.act, workspace=ws)
+    g.gemm_bf16_noalloc(p.M, p.N, p.K, p.alpha, d["A"], p.lda, p.layout_a, d["B"], p.ldb,
+                        p.layout_b, p.beta, d["C"], p.ldc, p.c_dtype, d["bias"], p.act)
+    torch.cuda.synchronize()
+    assert torch.equal(d["C"], c_ref), "gemm_bf16_noalloc differs from gemm_bf16"
+    out = d["C"].cpu().numpy()
+    return out.view(np.uint16) if p.c_dtype == OUT_BF16 else out
+
+
+def test_noalloc_two_calls_second_smaller():
+    big = synth.make_problem("bf16", 64, 4096, 4096, seed_base=0xD00000, beta=0.5, bias_std=0.1,
+                             act=ACT_GELU_ERF, c_dtype=OUT_BF16, a_std=1.0, b_std=0.02)
+    small = synth.make_problem("bf16", 40, 1024, 2048, seed_base=0xD01000, beta=0.5,
+                               bias_std=0.1, c_dtype=OUT_F32, a_std=1.0, b_std=0.02)
+    assert g.plan(64, 4096, 4096, False).split_k > 1 and g.plan(40, 1024, 2048, False).split_k > 1
+    for p in (big, small):
+        out = _both(p)
+        compare(p, out[:, :p.N])
+
+
+def test_noalloc_largest_workspace_and_unsplit():
+    # exactly the scratch size (32 MiB of partials), then a plan with no split
+    p = synth.make_problem("bf16", 512, 4096, 14336, seed_base=0xD02000, c_dtype=OUT_BF16,
+                           bias_std=0.1, a_std=1.0, b_std=0.02)
+    assert g.plan(512, 4096, 14336, False).workspace_bytes == 32 << 20
+    _both(p)
+    q = synth.make_problem("bf16", 300, 260, 192, seed_base=0xD03000, beta=0.5, c_dtype=OUT_F32)
+    assert g.plan(300, 260, 192, False).workspace_bytes == 0
+    compare(q, _both(q)[:, :q.N])
+
+
+def test_noalloc_refuses_workspace_beyond_scratch():
+    import torch
+    M, N, K = 1024, 4096, 14336
+    assert g.plan(M, N, K, False).workspace_bytes > 32 << 20
+    A = torch.zeros((M, K), dtype=torch.int16, device="cuda")
+    B = torch.zeros((N, K), dtype=torch.int16, device="cuda")
+    C = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    with pytest.raises(g.GemmError) as e:
+        g.gemm_bf16_noalloc(M, N, K, 1.0, A, K, synth.ROW, B, K, synth.COL, 0.0, C, N, OUT_F32)
+    assert e.value.status == 6  # GEMM_ERR_WORKSPACE_TOO_SMALL
+    torch.cuda.synchronize()
+    assert bool((C == 7.0).all()), "a refused call must not touch C"
