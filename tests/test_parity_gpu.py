@@ -324,3 +324,26 @@ def test_split_k_on_side_stream_binding_workspace():
     torch.cuda.synchronize()
     del junk
     compare(p, d["C"].cpu().numpy().view(np.uint16)[:, :N])
+
+
+def test_split_k_workspace_reused_across_shapes():
+    """One workspace serves split-K calls of different shapes in a row (fewer,
+    more, then fewer tiles): what a call leaves in it does not matter to the
+    next, so each call equals the same call on a fresh workspace bit for bit."""
+    import torch
+    shapes = [(40, 1024, 2048), (64, 4096, 4096), (100, 512, 8192), (40, 1024, 2048)]
+    need = max(g.workspace_size(M, N, K, False) for M, N, K in shapes)
+    shared = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for i, (M, N, K) in enumerate(shapes):
+        pl = g.plan(M, N, K, False)
+        assert pl.split_k > 1
+        print(f"[gpu] shared workspace M={M} N={N} K={K} split={pl.split_k}", flush=True)
+        p = synth.make_problem("bf16", M, N, K, seed_base=0xC20000 + i, beta=0.5, bias_std=0.1,
+                               c_dtype=OUT_F32, a_std=1.0, b_std=0.02)
+        d1, d2 = to_device(p), to_device(p)
+        fresh = torch.empty(pl.workspace_bytes, dtype=torch.uint8, device="cuda")
+        call(p, d1, workspace=shared)
+        call(p, d2, workspace=fresh)
+        torch.cuda.synchronize()
+        assert torch.equal(d1["C"], d2["C"])
+    compare(p, d1["C"].cpu().numpy()[:, :p.N])
