@@ -146,7 +146,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, bool fp8) {
   s.waves = 16;
   s.split = 1;
   s.k_split_len = static_cast<int>(K);
-  s.grid = (N + 15) / 16;
+  s.grid = skinny_streams(K) ? skinny_stream_grid(N) : (N + 15) / 16;
   return s;
 }
 

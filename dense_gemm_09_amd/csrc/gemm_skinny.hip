@@ -24,6 +24,8 @@
 // 16x16 MFMA accumulator layout: element e of lane l is row 4*(l/16) + e,
 // column l%16.
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -166,6 +168,119 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(GemmArgs p) {
   else skinny_epilogue<S, OUT, MB, ACT_GELU_TANH>(p, acc, n0, lane);
 }
 
+// Streaming variant, for K <= KW * KSM k-steps: one workgroup per CU walks the
+// 16-column blocks b = blockIdx.x, blockIdx.x + G, ... (G workgroups). The A
+// fragments of a wave's K range are the same for every block, so they are
+// loaded once into registers; B, the only operand that streams from HBM, is
+// loaded NBUF - 1 blocks ahead of the block being multiplied, so the loads of
+// later blocks are in flight while a block's partial sums are reduced across
+// the waves (in wave order 0..KW-1, as in the kernel above) and stored. The
+// reduction area is double-buffered, so one barrier per block suffices.
+template <bool FP8, int KW, int KSM, int NBUF, int OUT, int ACT>
+__global__ void __launch_bounds__(KW * 64) gemm_skinny_stream_kernel(GemmArgs p) {
+  using S = SkinnyCfg<FP8, 1, KW, 1>;
+  using Frag = typename std::conditional<FP8, i32x8, i32x4>::type;
+  __shared__ __attribute__((aligned(16))) f32x4 red[2][KW][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4;  // K group of this lane inside one MFMA
+  const int ksteps = (p.K + S::KSTEP - 1) / S::KSTEP;
+  const int per = (ksteps + KW - 1) / KW;  // k-steps per wave, <= KSM (checked on the host)
+  const int kb = wave * per * S::KSTEP;
+  const int ke = min(p.K, kb + per * S::KSTEP);
+  const int nblk = (p.N + 15) / 16;
+  const int G = gridDim.x;
+
+  // One MFMA's worth of a lane's operand row (16 or 32 bytes at element
+  // k0 + g * LANE_BYTES / ES); chunks at or past the wave's K end are zero.
+  auto ld = [&](const char* row, int k0, bool ok) {
+    Frag v = {};
+    const int k = k0 + g * (S::LANE_BYTES / S::ES);
+    const char* a = row + static_cast<int64_t>(k) * S::ES;
+    if (ok && k < ke) {
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(a);
+      v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+    }
+    if constexpr (FP8) {
+      if (ok && k + 16 < ke) {
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(a + 16);
+        v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+      }
+    }
+    return v;
+  };
+
+  // A: rows 0..15 (rows past M are zero lanes, never stored).
+  Frag av[KSM];
+  {
+    const int m = lane & 15;
+    const bool ok = m < p.M;
+    const char* arow = static_cast<const char*>(p.A) + static_cast<int64_t>(ok ? m : 0) * p.lda * S::ES;
+#pragma unroll
+    for (int ks = 0; ks < KSM; ++ks) av[ks] = ld(arow, kb + ks * S::KSTEP, ok && ks < per);
+  }
+  auto load_block = [&](int b, Frag (&bv)[KSM]) {
+    int n = 16 * b + (lane & 15);
+    n = n < p.N ? n : p.N - 1;  // columns past N are computed but never stored
+    const char* brow = static_cast<const char*>(p.B) + static_cast<int64_t>(n) * p.ldb * S::ES;
+#pragma unroll
+    for (int ks = 0; ks < KSM; ++ks) bv[ks] = ld(brow, kb + ks * S::KSTEP, ks < per);
+  };
+
+  Frag bv[NBUF][KSM];
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u)
+    if (static_cast<int>(blockIdx.x) + u * G < nblk) load_block(blockIdx.x + u * G, bv[u]);
+
+  for (int i0 = 0;; i0 += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int i = i0 + u;
+      const int b = blockIdx.x + i * G;
+      if (b >= nblk) return;
+      const int bn = b + (NBUF - 1) * G;  // prefetch: NBUF - 1 blocks ahead
+      if (bn < nblk) load_block(bn, bv[(u + NBUF - 1) % NBUF]);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSM; ++ks) {
+        if constexpr (FP8)
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[ks], bv[u][ks], acc, 0, 0, 0,
+                                                                 127, 0, 127);
+        else
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[ks]),
+                                                        __builtin_bit_cast(bf16x8_t, bv[u][ks]),
+                                                        acc, 0, 0, 0);
+      }
+      red[i & 1][wave][lane] = acc;
+      __syncthreads();
+      // Output (r, c) of the 16 x 16 block: MFMA lane 16 (r / 4) + c, element r % 4.
+      if (tid < 256) {
+        const int r = tid >> 4, c = tid & 15;
+        const int n = 16 * b + c;
+        if (r < p.M && n < p.N) {
+          const int src = 16 * (r >> 2) + c;
+          float z = red[i & 1][0][src][r & 3];
+#pragma unroll
+          for (int w = 1; w < KW; ++w) z += red[i & 1][w][src][r & 3];
+          if constexpr (S::ES == 1) z = z * (p.scale_a[r] * p.scale_b[n]);
+          z = p.alpha * z;
+          const int64_t off = static_cast<int64_t>(r) * p.ldc + n;
+          if constexpr (OUT == OUT_F32 || OUT == OUT_BF16) {
+            if (p.beta != 0.f) z += p.beta * load_cin1<OUT>(p.C, off);
+          }
+          if (p.bias) z += bf16_bits_to_f32(p.bias[n]);
+          z = apply_act<OUT>(z, ACT);
+          float qs, qz;
+          out_row_params<OUT>(p, r, qs, qz);
+          store_out1<OUT>(p.C, off, z, qs, qz);
+        }
+      }
+    }
+  }
+}
+
 #ifndef G355_KERNELS_ONLY
 // KW = 16 K-split waves per workgroup; U k-steps of loads in flight per wave
 // (BF16 4 x 1 KB, FP8 2 x 2 KB). Chosen by a sweep at K = 4096, N = 4096..18432.
@@ -185,10 +300,47 @@ static hipError_t launch_mb(const GemmArgs& a, int out, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The streaming variant: 16 K-split waves, at most KSM k-steps each (K up to
+// 4096 for both types), B prefetched NBUF - 1 blocks ahead. Measured at
+// K = 4096 against the one-block-per-workgroup kernel above: FP8 M = 1,
+// N = 18432 22.3 -> 18.8 us, M = 16 28.3 -> 20.1 us, BF16 M = 16 42.5 -> 35.5 us
+// (M = 1 BF16 was already at ~5 TB/s: unchanged). Prefetching four FP8 blocks
+// ahead instead of two needs more than the 128 VGPRs a 16-wave workgroup may
+// use and spills (27 us).
+template <bool FP8, int OUT>
+static hipError_t launch_stream_out(const GemmArgs& a, hipStream_t stream) {
+  constexpr int KW = 16, KSM = FP8 ? 2 : 8, NBUF = FP8 ? 3 : 2;
+  const dim3 grid(static_cast<unsigned>(skinny_stream_grid(a.N))), block(KW * 64);
+  if (a.act == ACT_NONE)
+    hipLaunchKernelGGL((gemm_skinny_stream_kernel<FP8, KW, KSM, NBUF, OUT, ACT_NONE>), grid, block,
+                       0, stream, a);
+  else if (a.act == ACT_RELU)
+    hipLaunchKernelGGL((gemm_skinny_stream_kernel<FP8, KW, KSM, NBUF, OUT, ACT_RELU>), grid, block,
+                       0, stream, a);
+  else if (a.act == ACT_GELU_ERF)
+    hipLaunchKernelGGL((gemm_skinny_stream_kernel<FP8, KW, KSM, NBUF, OUT, ACT_GELU_ERF>), grid,
+                       block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_skinny_stream_kernel<FP8, KW, KSM, NBUF, OUT, ACT_GELU_TANH>), grid,
+                       block, 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool FP8>
+static hipError_t launch_stream(const GemmArgs& a, int out, hipStream_t stream) {
+  if (out == OUT_BF16) return launch_stream_out<FP8, OUT_BF16>(a, stream);
+  if (out == OUT_I8) return launch_stream_out<FP8, OUT_I8>(a, stream);
+  if (out == OUT_E4M3) return launch_stream_out<FP8, OUT_E4M3>(a, stream);
+  return launch_stream_out<FP8, OUT_F32>(a, stream);
+}
+
 hipError_t launch_skinny(const Plan& plan, const LaunchSpec& spec, const GemmArgs& a,
                          hipStream_t stream) {
   (void)plan;
   if (a.M > 16) return hipErrorInvalidValue;  // the plan only selects M <= 16
+  if (skinny_streams(a.K))
+    return spec.fp8 ? launch_stream<true>(a, spec.out, stream)
+                    : launch_stream<false>(a, spec.out, stream);
   return spec.fp8 ? launch_mb<true, 1>(a, spec.out, stream)
                   : launch_mb<false, 1>(a, spec.out, stream);
 }

@@ -66,6 +66,13 @@ hipError_t launch_tile(const Plan& plan, const LaunchSpec& spec, const GemmArgs&
                        hipStream_t stream);
 hipError_t launch_skinny(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
                          hipStream_t stream);
+// The skinny kernel's streaming variant covers K up to 16 waves x 4096/16
+// elements; its grid is one workgroup per CU at most.
+inline bool skinny_streams(int64_t K) { return K <= 4096; }
+inline int64_t skinny_stream_grid(int64_t N) {
+  const int64_t blocks = (N + 15) / 16;
+  return blocks < 256 ? blocks : 256;
+}
 hipError_t launch_splitk_reduce(const Plan& plan, const LaunchSpec& spec, const GemmArgs& args,
                                 hipStream_t stream);
 
