@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB device copy (counter "
                          "calibration) then 3 launches of each headline GEMM")
+    ap.add_argument("--pmc-decode", action="store_true",
+                    help="short run for rocprofv3 --pmc: a 256 MiB device copy (counter "
+                         "calibration) then the FP8 and BF16 decode GEMMs M=1, N=18432, K=4096 "
+                         "over their rotating buffer sets, each set used twice")
     ap.add_argument("--only", default="", help="comma list of extra groups: decode,ffn,ragged,proj,quant,qout,mx,pack")
     return ap.parse_args()
 
@@ -284,6 +288,27 @@ def pmc_run(p_bf16, p_fp8):
         f"{len(w_bf16.sets)} sets, {n} x fp8 4096^3 over {len(w_fp8.sets)} sets")
 
 
+def pmc_decode():
+    """Known-size copy, then the M=1, N=18432 decode GEMMs over rotating buffer
+    sets (after the first round every launch reads weights that are not in the
+    caches)."""
+    import torch
+    from synth import workloads
+    src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    for kind in ("fp8", "bf16"):
+        w = Workload(workloads.decode(kind, 1, 18432), copies_for(workloads.decode(kind, 1, 18432)))
+        for _ in range(2 * len(w.sets)):
+            w()
+        torch.cuda.synchronize()
+        log(f"[bench] pmc decode: {2 * len(w.sets)} x {kind} 1x18432x4096 over {len(w.sets)} sets")
+        del w
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     global NO_ROTATE
@@ -298,6 +323,9 @@ def main():
     g.lib()  # fail loudly if the HIP library is missing
     torch.cuda.init()
 
+    if args.pmc_decode:
+        pmc_decode()
+        return
     log("[bench] generating inputs")
     p_bf16 = workloads.square_bf16(4096)
     p_fp8 = workloads.fp8_projection(4096, 4096, 4096, sub=1)

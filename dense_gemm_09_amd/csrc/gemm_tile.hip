@@ -396,34 +396,44 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
   // outputs have no C_in.
   constexpr bool HAS_CIN = !SPLIT && (OUT == OUT_F32 || OUT == OUT_BF16);
   // Double-buffered C_in, except where the FP32 C_in of a 256-wide FP8 tile
-  // would not fit next to its accumulators (it is then loaded per strip).
+  // would not fit next to its accumulators (it is then loaded per strip). A
+  // BF16 C_in is held as its packed bits (two registers per four elements) and
+  // widened where it is used.
   constexpr int CIN_BUFS = (C::FP8 && OUT == OUT_F32 && C::FN * C::FM >= 8) ? 1 : 2;
-  float4 cin[CIN_BUFS][E::ITERS];
-  auto load_cin = [&](int i, float4 (&dst)[E::ITERS]) {
+  using CinT = std::conditional_t<OUT == OUT_BF16, u32x2, float4>;
+  CinT cin[CIN_BUFS][E::ITERS];
+  auto load_cin = [&](int i, CinT (&dst)[E::ITERS]) {
 #pragma unroll
     for (int it = 0; it < E::ITERS; ++it) {
       const int m = row0 + 32 * i + it * E::RPI + rq;
-      dst[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (OUT == OUT_BF16) dst[it] = u32x2{0u, 0u};
+      else dst[it] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (m >= M) continue;
       const int64_t off = static_cast<int64_t>(m) * p.ldc + n;
-      if (vec_ok) {
-        // C_in is read once (non-temporal, like the stores of C).
-        if constexpr (OUT == OUT_BF16) {
-          const u32x2 h = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p.C) + off));
-          dst[it] = make_float4(__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xffff0000u),
-                                __uint_as_float(h.y << 16), __uint_as_float(h.y & 0xffff0000u));
+      if constexpr (OUT == OUT_BF16) {
+        const uint16_t* c16 = static_cast<const uint16_t*>(p.C) + off;
+        if (vec_ok) {
+          // C_in is read once (non-temporal, like the stores of C).
+          dst[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(c16));
         } else {
+          unsigned h[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) h[q] = c16[q];
+          dst[it] = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        }
+      } else {
+        if (vec_ok) {
           const f32x4 c = __builtin_nontemporal_load(
               reinterpret_cast<const f32x4*>(static_cast<const float*>(p.C) + off));
           dst[it] = make_float4(c[0], c[1], c[2], c[3]);
-        }
-      } else {
-        float t[4] = {0.f, 0.f, 0.f, 0.f};
+        } else {
+          float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (n + q < N) t[q] = load_cin1<OUT>(p.C, off + q);
-        dst[it] = make_float4(t[0], t[1], t[2], t[3]);
+          for (int q = 0; q < 4; ++q)
+            if (n + q < N) t[q] = load_cin1<OUT>(p.C, off + q);
+          dst[it] = make_float4(t[0], t[1], t[2], t[3]);
+        }
       }
     }
   };
@@ -514,8 +524,20 @@ __device__ __forceinline__ void epilogue(const GemmArgs& p, const f32x16 (&acc)[
           for (int q = 0; q < 4; ++q) v[q] = fmaf(v[q], cs[q], bias_v[q]);
         }
         if constexpr (HAS_CIN) {
-          const float4 cc = cin[CIN_BUFS == 2 ? (i & 1) : 0][it];
-          const float c4[4] = {cc.x, cc.y, cc.z, cc.w};
+          float c4[4];
+          if constexpr (OUT == OUT_BF16) {
+            const u32x2 h = cin[CIN_BUFS == 2 ? (i & 1) : 0][it];
+            c4[0] = __uint_as_float(h.x << 16);
+            c4[1] = __uint_as_float(h.x & 0xffff0000u);
+            c4[2] = __uint_as_float(h.y << 16);
+            c4[3] = __uint_as_float(h.y & 0xffff0000u);
+          } else {
+            const float4 cc = cin[CIN_BUFS == 2 ? (i & 1) : 0][it];
+            c4[0] = cc.x;
+            c4[1] = cc.y;
+            c4[2] = cc.z;
+            c4[3] = cc.w;
+          }
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             if (use_c) v[q] = fmaf(p.beta, c4[q], v[q]);

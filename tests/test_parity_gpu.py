@@ -72,6 +72,21 @@ def test_padded_leading_dims_with_nan_padding(kind):
 
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8"])
+@pytest.mark.parametrize("M,N,K,ldc", [(3000, 3000, 256, 3000), (3000, 3001, 256, 3003),
+                                       (300, 700, 384, 701)],
+                         ids=["256x256-vector", "256x256-element", "128x128-element"])
+def test_bf16_c_in(kind, M, N, K, ldc):
+    # BF16 C_in read by the tile epilogue (beta != 0), held as packed bits until
+    # it is used: rows 16-byte aligned (vector loads), and an odd ldc with a
+    # ragged N (element loads; NaN padding past N).
+    assert g.plan(M, N, K, kind == "fp8").tile_m == (256 if M == 3000 else 128)
+    p = synth.make_problem(kind, M, N, K, seed_base=0x320000 + N + ldc, beta=-0.75, ldc=ldc,
+                           bias_std=0.25, act=ACT_GELU_ERF, c_dtype=OUT_BF16, a_std=1.0,
+                           b_std=0.06)
+    compare(p, run(p))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
 def test_unaligned_base_pointers(kind):
     import torch
     M, N, K = 150, 140, 256
