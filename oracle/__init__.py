@@ -6,11 +6,15 @@ it: the two meet only in the seeded inputs (package `synth`) they both read.
 
 What it computes (in float64, the plain definition written out):
 
-    acc[m, n] = sum_k a(m, k) * b(k, n)                 (float64)
+    acc[m, n] = sum_k a(m, k) * b(k, n)                 (float64, k ascending)
     dq        = scale_a[m] * scale_b[n] * acc           (FP8 variant only)
     z         = alpha * dq + beta * C_in[m, n] + bias[n]
     y         = act(z)
     out       = round_to_nearest_even(y) in FP32 or BF16 (single rounding)
+
+The sum over k is a plain i-k-j triple loop in C (triple_loop.c, compiled by
+native.py with gcc, no contraction into FMAs, OpenMP over output rows): each
+acc[m, n] is accumulated in ascending k, one float64 add per term.
 
 Sources: the GEMM definition C = alpha*A*B + beta*C with A MxK, B KxN (first
 DeepGEMM page, sec. 1.1); FP32-or-better accumulation of 16-bit inputs (same
@@ -29,9 +33,17 @@ of x * scale, first DeepGEMM page, sec. 6.2) is in qout.py; the block-scaled
 
 Parity status: every function here is pinned by the `-m "not gpu"` tests in
 tests/test_oracle.py, tests/test_oracle_quant.py, tests/test_oracle_qout.py and
-tests/test_oracle_mx.py (codec tables, rounding ties, integer-valued exact
-products, identity and permutation matrices, closed forms, linearity, GELU
-against tabulated normal-CDF values). No function is "parity unpinned".
+tests/test_oracle_mx.py: codec tables against the formats' named values,
+rounding ties, integer-valued products (exact), tiny dyadic operands against
+rational arithmetic, the ascending-k order of the float64 sum, identity and
+permutation matrices, alpha scaling the product only (alpha = 2, beta = 3,
+C_in = AB, bias b gives exactly 5AB + b), the activation applied after
+beta*C_in and the bias, GELU against tabulated normal-CDF values, a
+high-precision (decimal) tanh form and the normal tail series, and planted
+mistakes (a dropped K term, a transposed B, a flipped beta, a shifted bias,
+alpha applied to the bias or to beta*C_in, the activation applied before
+beta*C_in or the bias) rejected by the parity tolerance. No function is
+"parity unpinned".
 """
 from .codecs import (decode_bf16, decode_e4m3, round_to_bf16, round_to_bf16_bits,
                      round_to_f32)
