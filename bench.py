@@ -300,7 +300,8 @@ def pmc_decode():
     dst.copy_(src)
     torch.cuda.synchronize()
     for kind in ("fp8", "bf16"):
-        w = Workload(workloads.decode(kind, 1, 18432), copies_for(workloads.decode(kind, 1, 18432)))
+        p = workloads.decode(kind, 1, 18432)
+        w = Workload(p, copies_for(p))
         for _ in range(2 * len(w.sets)):
             w()
         torch.cuda.synchronize()
