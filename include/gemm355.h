@@ -17,8 +17,9 @@
  * Conventions common to every entry point
  * ---------------------------------------
  * - All matrix, vector and workspace pointers are DEVICE pointers owned by the
- *   caller. The library never allocates, frees or synchronises, and keeps no
- *   mutable global state: calls are reentrant and may run on any stream.
+ *   caller. The library never allocates, frees or synchronises, and apart
+ *   from the scratch array of gemm_bf16_noalloc keeps no mutable global
+ *   state: the other calls are reentrant and may run on any stream.
  * - Operand layouts (per operand, gemm_layout):
  *     A ROW: a(m,k) = A[m*lda + k], lda >= K      A COL: a(m,k) = A[k*lda + m], lda >= M
  *     B ROW: b(k,n) = B[k*ldb + n], ldb >= N      B COL: b(k,n) = B[n*ldb + k], ldb >= K
@@ -30,7 +31,10 @@
  * - Rounding: FP32 accumulation; epilogue arithmetic in FP32; the BF16 output
  *   cast rounds to nearest even.
  * - Activations: ReLU max(z,0); GELU_ERF z*Phi(z) = 0.5 z (1 + erf(z/sqrt 2));
- *   GELU_TANH 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+ *   GELU_TANH 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))). Both GELUs are
+ *   evaluated in forms without cancellation, so they keep their relative
+ *   accuracy for large negative z: within 2^-19 relative (+1 ulp) of the exact
+ *   value for FP32 output, within one BF16 ulp for BF16 output.
  * - Quick returns: M == 0 or N == 0 returns GEMM_OK and launches nothing.
  *   K == 0 gives C = act(beta*C + bias). beta == 0 means C is not read (NaN in
  *   C is ignored).
@@ -277,7 +281,8 @@ size_t gemm_workspace_size(int64_t M, int64_t N, int64_t K, int is_fp8);
  * GEMM_ERR_BAD_DIM / GEMM_ERR_NULL_POINTER. Intended for tests and tuning.
  */
 typedef struct {
-  int32_t kernel;       /* 0 = tiled MFMA kernel, 1 = split-K skinny kernel */
+  int32_t kernel;       /* 0 = tiled MFMA kernel, 1 = skinny weight-streaming kernel
+                           (M <= 16; K split over the waves of a workgroup) */
   int32_t tile_m, tile_n, tile_k;
   int32_t split_k;      /* number of K partitions (1 = none) */
   int32_t waves;        /* wavefronts per workgroup */
