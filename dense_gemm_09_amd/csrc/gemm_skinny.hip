@@ -176,6 +176,18 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_kernel(GemmArgs p) {
 // later blocks are in flight while a block's partial sums are reduced across
 // the waves (in wave order 0..KW-1, as in the kernel above) and stored. The
 // reduction area is double-buffered, so one barrier per block suffices.
+// When the blocks do not divide into whole rounds of G and the last round
+// holds at most G/2 of them, each of those can be split into two 8-column
+// halves on two workgroups (the MFMA's other 8 columns get zero weights and
+// are not stored): that round then moves half a block per workgroup instead
+// of one block on half of them (N = 18432: 4.5 rounds instead of 5). Every
+// output column is computed exactly as in a whole block.
+// The last round is split for BF16 only: measured at K = 4096, it takes BF16
+// M = 1 / 16, N = 18432 from 30.1 / 35.0 to 28.9 / 33.2 us, and leaves FP8
+// (19 us, whose rate is not set by that round) where it was.
+template <bool FP8>
+constexpr bool kSplitLastRound = !FP8;
+
 template <bool FP8, int KW, int KSM, int NBUF, int OUT, int ACT>
 __global__ void __launch_bounds__(KW * 64) gemm_skinny_stream_kernel(GemmArgs p) {
   using S = SkinnyCfg<FP8, 1, KW, 1>;
@@ -221,27 +233,61 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_stream_kernel(GemmArgs p)
 #pragma unroll
     for (int ks = 0; ks < KSM; ++ks) av[ks] = ld(arow, kb + ks * S::KSTEP, ok && ks < per);
   }
-  auto load_block = [&](int b, Frag (&bv)[KSM]) {
-    int n = 16 * b + (lane & 15);
+  // Work item i of this workgroup: its column range [col0, col0 + width).
+  // Items 0..R-1 are the whole blocks blockIdx.x + i G; item R is its share
+  // of the last, partial round (T blocks), whole or halved as described above.
+  const int R = nblk / G, T = nblk - R * G;
+  const bool halves = kSplitLastRound<FP8> && T > 0 && 2 * T <= G;
+  const int bx = blockIdx.x;
+  auto item = [&](int i, int& col0, int& width) -> bool {
+    width = 16;
+    if constexpr (!kSplitLastRound<FP8>) {
+      const int b = bx + i * G;
+      col0 = 16 * b;
+      return b < nblk;
+    }
+    if (i < R) {
+      col0 = 16 * (bx + i * G);
+      width = 16;
+      return true;
+    }
+    if (i > R || T == 0) return false;
+    if (halves) {
+      if (bx >= 2 * T) return false;
+      col0 = 16 * (R * G + (bx >> 1)) + 8 * (bx & 1);
+      width = 8;
+      return col0 < p.N;
+    }
+    if (bx >= T) return false;
+    col0 = 16 * (R * G + bx);
+    width = 16;
+    return true;
+  };
+  auto load_block = [&](int col0, int width, Frag (&bv)[KSM]) {
+    const int c = lane & 15;
+    int n = col0 + c;
     n = n < p.N ? n : p.N - 1;  // columns past N are computed but never stored
     const char* brow = static_cast<const char*>(p.B) + static_cast<int64_t>(n) * p.ldb * S::ES;
+    const bool in = !kSplitLastRound<FP8> || c < width;
 #pragma unroll
-    for (int ks = 0; ks < KSM; ++ks) bv[ks] = ld(brow, kb + ks * S::KSTEP, ks < per);
+    for (int ks = 0; ks < KSM; ++ks) bv[ks] = ld(brow, kb + ks * S::KSTEP, in && ks < per);
   };
 
   Frag bv[NBUF][KSM];
 #pragma unroll
-  for (int u = 0; u < NBUF - 1; ++u)
-    if (static_cast<int>(blockIdx.x) + u * G < nblk) load_block(blockIdx.x + u * G, bv[u]);
+  for (int u = 0; u < NBUF - 1; ++u) {
+    int c0, w0;
+    if (item(u, c0, w0)) load_block(c0, w0, bv[u]);
+  }
 
   for (int i0 = 0;; i0 += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
       const int i = i0 + u;
-      const int b = blockIdx.x + i * G;
-      if (b >= nblk) return;
-      const int bn = b + (NBUF - 1) * G;  // prefetch: NBUF - 1 blocks ahead
-      if (bn < nblk) load_block(bn, bv[(u + NBUF - 1) % NBUF]);
+      int col0, width;
+      if (!item(i, col0, width)) return;
+      int cn, wn;  // prefetch: NBUF - 1 items ahead
+      if (item(i + NBUF - 1, cn, wn)) load_block(cn, wn, bv[(u + NBUF - 1) % NBUF]);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KSM; ++ks) {
@@ -258,8 +304,8 @@ __global__ void __launch_bounds__(KW * 64) gemm_skinny_stream_kernel(GemmArgs p)
       // Output (r, c) of the 16 x 16 block: MFMA lane 16 (r / 4) + c, element r % 4.
       if (tid < 256) {
         const int r = tid >> 4, c = tid & 15;
-        const int n = 16 * b + c;
-        if (r < p.M && n < p.N) {
+        const int n = col0 + c;
+        if (r < p.M && (!kSplitLastRound<FP8> || c < width) && n < p.N) {
           const int src = 16 * (r >> 2) + c;
           float z = red[i & 1][0][src][r & 3];
 #pragma unroll

@@ -183,6 +183,19 @@ def test_skinny_kernel(kind, M, N, K):
 
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8"])
+@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("N", [5696, 5691, 6160, 18432])
+def test_skinny_last_round(kind, M, N):
+    # More 16-column blocks than workgroups (256): 5696 and 18432 leave a last
+    # round of at most 128 blocks, each split into two 8-column halves (5691:
+    # its last half holds 3 columns); 6160 leaves 129 blocks, run whole.
+    assert g.plan(M, N, 4096, kind == "fp8").kernel == 1
+    p = synth.make_problem(kind, M, N, 4096, seed_base=0x840000 + M + N, beta=0.5, bias_std=0.1,
+                           act=ACT_GELU_ERF, c_dtype=OUT_BF16, a_std=1.0, b_std=0.02)
+    compare(p, run(p))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
 def test_skinny_fp32_out_and_fallback(kind):
     # fp32 output on the skinny kernel, and an unaligned ld that falls back to the tile kernel
     p = synth.make_problem(kind, 5, 300, 512, seed_base=0x830000, c_dtype=OUT_F32, beta=1.0)
