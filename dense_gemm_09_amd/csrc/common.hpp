@@ -171,6 +171,24 @@ __device__ __forceinline__ float erfc_cheb_poly(float t) {
   return p;
 }
 
+// Q(t) = log2(e) P(t) + 63 for the same t = 1 / (1 + x/2), as one degree-7
+// polynomial: a least-squares fit over t in [1/7, 1] (x <= 12), within 2e-6
+// of Q there (dense_gemm_09_amd/gelu_fit.py makes the table). The 2^63 keeps
+// 2^Q e^(-x^2) normal far into GELU's negative tail; the caller scales by
+// 2^-64, which also supplies GELU's factor 1/2. Used for BF16 and quantised
+// outputs, where it is accurate well below half a BF16 ulp.
+__device__ __forceinline__ float erfc_log2_fit7(float t) {
+  float q = -0.27580565214157104f;
+  q = fmaf(q, t, 1.1046985387802124f);
+  q = fmaf(q, t, -1.4792454242706299f);
+  q = fmaf(q, t, 0.5366070866584778f);
+  q = fmaf(q, t, -0.07367606461048126f);
+  q = fmaf(q, t, 0.5731409788131714f);
+  q = fmaf(q, t, 1.439933180809021f);
+  q = fmaf(q, t, 61.174346923828125f);
+  return q;
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTwoM64 = 5.42101086242752217e-20f;  // 2^-64
 
@@ -192,25 +210,26 @@ __device__ __forceinline__ float exp2_split(double q, int& n) {
 // down into FP32's subnormal range (erfc alone, smaller by |z|/2, would
 // underflow first). The exponent P - z^2/2 is one fused multiply-add from z
 // itself (z/2 is exact). PRECISE forms it in double and splits off its power
-// of two exactly (relative error ~5e-7 for every z; FP32 outputs); otherwise
-// it is scaled by 2^64 inside the exponential and 2^-64 at the end, and its
-// FP32 rounding leaves a relative error of up to ~1e-5 at the far negative
-// end, far below a BF16 ulp.
+// of two exactly (relative error ~5e-7 for every z; FP32 outputs). Otherwise
+// (BF16 and quantised outputs) the exponent is log2(e) (P - z^2/2) + 63 from
+// the fitted Q(t) and one fused multiply-add, the result is scaled by 2^-64
+// at the end, and the FP32 roundings leave a relative error of up to ~1e-5
+// at the far negative end, far below a BF16 ulp.
 template <bool PRECISE>
 __device__ __forceinline__ float gelu_erf(float z) {
-  const float hz = 0.5f * z;
-  const float x = fabsf(z) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.5f, x, 1.f));
-  const float p = erfc_cheb_poly(t);
+  // t = 1 / (1 + x/2), x = |z| / sqrt 2
+  const float t = __builtin_amdgcn_rcpf(fmaf(fabsf(z), 0.35355339059327376f, 1.f));
   float w;
   if constexpr (PRECISE) {
+    const float hz = 0.5f * z;
+    const float p = erfc_cheb_poly(t);
     const double zd = z;
     int n;
     const float r = exp2_split((static_cast<double>(p) - 0.5 * zd * zd) * 1.4426950408889634074, n);
     w = __builtin_ldexpf(hz * t * r, n);
   } else {
-    const float r = __builtin_amdgcn_exp2f(fmaf(fmaf(-hz, z, p), kLog2e, 64.f));
-    w = (hz * t * r) * kTwoM64;
+    const float r = __builtin_amdgcn_exp2f(fmaf(z * z, -0.5f * kLog2e, erfc_log2_fit7(t)));
+    w = (z * t * r) * kTwoM64;
   }
   return z < 0.f ? w : z - w;
 }
